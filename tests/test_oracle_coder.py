@@ -1,0 +1,292 @@
+"""Pins for the oracle's range coder, stream layout and coded size (no GPU)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import ndtr
+
+from oracle import skvref as R
+from lossless_kv_cache_scalar_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rc_bigint(pairs):
+    """The coder's definition on unbounded integers: no carry logic at all."""
+    L, Rg, n = 0, 2 ** 48 - 1, 0
+    for c, f in pairs:
+        r = Rg >> 24
+        L += r * c
+        Rg = r * f
+        while Rg < 2 ** 40:
+            L <<= 8
+            Rg <<= 8
+            n += 1
+    L = -(-L // 2 ** 40) * 2 ** 40
+    return (L >> 40).to_bytes(n + 1, "big")
+
+
+def test_rc_hand_examples():
+    with open(os.path.join(GOLDEN, "rc_hand.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for case in cases:
+        c = [p[0] for p in case["pairs"]]
+        f = [p[1] for p in case["pairs"]]
+        assert R.rc_encode_seq(c, f).hex() == case["bytes"], case["why"]
+        assert rc_bigint(case["pairs"]).hex() == case["bytes"]
+
+
+def _random_pairs(rng, n, mode):
+    T = 1 << 24
+    if mode == "uniform":
+        f = rng.integers(1, T // 16, n)
+    elif mode == "skewed":
+        f = np.maximum(1, (T * rng.random(n) ** 6).astype(np.int64))
+    else:  # near the top of the interval, small f: many carries and 0xff runs
+        f = rng.integers(1, 1 << 10, n)
+    c = (rng.random(n) * (T - f)).astype(np.int64)
+    if mode == "top":
+        c = T - f - rng.integers(0, 1 << 12, n)
+        c = np.maximum(c, 0)
+    return c, f
+
+
+@pytest.mark.parametrize("mode", ["uniform", "skewed", "top"])
+def test_rc_matches_unbounded_integer_definition(mode):
+    rng = np.random.default_rng(hash(mode) % 2 ** 32)
+    carries_through_ff = 0
+    for trial in range(300):
+        n = int(rng.integers(0, 200))
+        c, f = _random_pairs(rng, n, mode)
+        want = rc_bigint(list(zip(c.tolist(), f.tolist())))
+        got = R.rc_encode_seq(c, f)
+        assert got == want, (mode, trial)
+        if b"\x00\x00" in got[:-1]:
+            carries_through_ff += 1
+    if mode == "top":
+        assert carries_through_ff > 0  # the carry path was exercised
+
+
+def _cache(w, seed=None, tokens=None):
+    x, mu = synth.generate(w, seed=seed, tokens=tokens)
+    xn = x.numpy().view(np.uint16 if w.sym_fmt == 0 else np.uint8)
+    mun = mu.numpy().view(np.uint16) if w.mu_fmt == 0 else mu.numpy()
+    return np.ascontiguousarray(xn), np.ascontiguousarray(mun)
+
+
+def _calibrate(w, nseq=1):
+    cal = R.Calibrator(R.make_shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt))
+    for j in range(nseq):
+        cx, cm = _cache(w.with_tokens(w.calib_tokens), seed=w.calib_seed(j))
+        cal.accumulate(cx, cm)
+    return cal.finalize()
+
+
+def _shape(w):
+    return R.make_shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+
+
+def test_roundtrip_every_bf16_pattern():
+    """decode(encode(x)) == x for all 65536 bf16 patterns (NaN, inf, -0 included),
+    with random, non-finite and zero predictor means and sigma = 0 channels."""
+    rng = np.random.default_rng(7)
+    sh = R.make_shape(1, 1, 512, 64, R.SYM_BF16, R.MU_BF16)
+    x = rng.permutation(65536).astype(np.uint16).reshape(1, 2, 1, 512, 64)
+    mu = (x.astype(np.int64) + rng.integers(-40, 40, x.shape)).clip(0, 65535).astype(np.uint16)
+    mu.reshape(-1)[::101] = 0x7FC0  # NaN predictions
+    mu.reshape(-1)[::103] = 0xFF80  # -inf predictions
+    sigma = np.exp(rng.uniform(-30, 30, 2 * 64)).astype(np.float32)
+    sigma[::9] = 0.0
+    hist = rng.integers(0, 50, 65536).astype(np.uint64)
+    m = R.Model(0, hist)
+    bits, offs = m.encode(sh, x, mu, sigma)
+    out, st = m.decode(sh, bits, offs, mu, sigma)
+    assert st == R.OK
+    np.testing.assert_array_equal(out, x)
+
+
+def test_roundtrip_every_e4m3_pattern():
+    rng = np.random.default_rng(8)
+    sh = R.make_shape(1, 2, 300, 64, R.SYM_E4M3, R.MU_F32)
+    n = 2 * 2 * 300 * 64
+    x = np.tile(np.arange(256, dtype=np.uint8), n // 256 + 1)[:n]
+    x = rng.permutation(x).reshape(1, 2, 2, 300, 64)
+    vals = np.array([R.value(1, int(v)) for v in range(256)])
+    base = np.nan_to_num(vals[x], nan=0.0)
+    mu = (base + rng.standard_normal(x.shape) * np.exp(rng.uniform(-6, 6, x.shape))).astype(np.float32)
+    mu.reshape(-1)[::37] = np.nan
+    sigma = np.exp(rng.uniform(-10, 6, 2 * 2 * 64)).astype(np.float32)
+    sigma[::5] = 0.0
+    m = R.Model(1, rng.integers(0, 1000, 256).astype(np.uint64))
+    bits, offs = m.encode(sh, x, mu, sigma)
+    out, st = m.decode(sh, bits, offs, mu, sigma)
+    assert st == R.OK
+    np.testing.assert_array_equal(out, x)
+
+
+@pytest.mark.parametrize("tokens,head_dim", [(1, 64), (3, 128), (300, 64), (300, 128), (257, 8), (40, 512)])
+def test_roundtrip_ragged_chunks(tokens, head_dim):
+    rng = np.random.default_rng(tokens * 1000 + head_dim)
+    w = synth.Workload("t", 1, 2, 2, head_dim, tokens, 0, 0, 0.02, 1, 64)
+    x, mu = _cache(w)
+    sigma = (0.02 * np.exp(rng.standard_normal(w.n_channels))).astype(np.float32)
+    m = R.Model(0)
+    sh = _shape(w)
+    bits, offs = m.encode(sh, x, mu, sigma)
+    assert len(offs) == R.num_chunks(sh) + 1
+    out, st = m.decode(sh, bits, offs, mu, sigma)
+    assert st == R.OK
+    np.testing.assert_array_equal(out, x)
+    # every lane has at least its flush byte, even with no symbols
+    for c in range(len(offs) - 1):
+        lens = np.frombuffer(bits[int(offs[c]):int(offs[c]) + 128].tobytes(), dtype="<u2")
+        assert lens.min() >= 1 and int(offs[c + 1] - offs[c]) == 128 + int(lens.sum())
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_pure_noise_stream_lengths(fmt):
+    """With every frequency 256/T each bf16 symbol takes exactly 2 bytes and
+    each e4m3 symbol 1 byte, plus one flush byte per substream."""
+    w = synth.Workload("t", 1, 1, 2, 64, 300, fmt, 0, 0.02, 1, 64)
+    x, mu = _cache(w)
+    N, T = (65536, 1 << 24) if fmt == 0 else (256, 1 << 16)
+    m = R.Model(fmt, None, MG=0, Mp=T - N)
+    sh = _shape(w)
+    bits, offs = m.encode(sh, x, mu, np.ones(w.n_channels, np.float32))
+    for c in range(len(offs) - 1):
+        lens = np.frombuffer(bits[int(offs[c]):int(offs[c]) + 128].tobytes(), dtype="<u2").astype(int)
+        tok = min(256, w.tokens - 256 * (c % 2))
+        groups = tok * w.head_dim // 8
+        n_lane = np.array([8 * len(range(l, groups, 64)) for l in range(64)])
+        np.testing.assert_array_equal(lens, (2 if fmt == 0 else 1) * n_lane + 1)
+    out, st = m.decode(sh, bits, offs, mu, np.ones(w.n_channels, np.float32))
+    assert st == R.OK and np.array_equal(out, x)
+
+
+def _exact_neglog2(fmt, x, mu, sigma_per_scalar, hist):
+    """-log2 of the real-valued mixture integrated over each symbol's bin (fp64)."""
+    lo, hi = R.bins(fmt, x.astype(np.uint32).ravel())
+    lo = lo.astype(np.float64)
+    hi = hi.astype(np.float64)
+    m = np.nan_to_num(mu.astype(np.float64).ravel(), nan=0.0, posinf=0.0, neginf=0.0)
+    s = sigma_per_scalar.astype(np.float64).ravel()
+
+    def mass(scale):
+        a = (lo - m) / scale
+        b = (hi - m) / scale
+        upper = a > 0
+        return np.where(upper, ndtr(-a) - ndtr(-b), ndtr(b) - ndtr(a))
+
+    h = hist.astype(np.float64) + 1
+    p = h[x.astype(np.int64).ravel()] / h.sum()
+    q = 0.95 * mass(s) + 0.03 * mass(3 * s) + 0.02 * p
+    return -np.log2(q)
+
+
+@pytest.mark.parametrize("name", ["tiny_bf16", "qwen3_0.6b_e4m3"])
+def test_coded_size_within_bound_of_exact_mixture(name):
+    """Cost per symbol is -log2 q(x) ('Speculative KV coding', the KV cache is
+    not really random: every bit spent is cross-entropy).  Coded bytes stay
+    within 0.5% + 8 bytes per substream of the real-valued mixture's ideal."""
+    w = synth.WORKLOADS[name]
+    if w.layers > 1:
+        w = w.with_tokens(512, layers=2)
+    sigma, hist = _calibrate(w)
+    x, mu = _cache(w)
+    m = R.Model(w.sym_fmt, hist)
+    bits, offs = m.encode(_shape(w), x, mu, sigma)
+    mu_f = mu.view(np.uint16).astype(np.uint32) << 16 if w.mu_fmt == 0 else mu
+    mu_f = np.ascontiguousarray(mu_f).view(np.float32) if w.mu_fmt == 0 else mu_f
+    sig = np.broadcast_to(sigma.reshape(w.layers, 2, w.kv_heads, 1, w.head_dim), x.shape)
+    ideal_bits = _exact_neglog2(w.sym_fmt, x, mu_f, sig, hist).sum()
+    n_sub = 64 * (len(offs) - 1)
+    assert len(bits) <= 1.005 * ideal_bits / 8 + 8 * n_sub
+    # and the integer model's own ideal is within 0.5% of the real one
+    s = np.broadcast_to(R.scale(sigma).reshape(w.layers, 2, w.kv_heads, 1, w.head_dim), x.shape)
+    clo, chi = m.cum_pair(mu_f.ravel(), np.ascontiguousarray(s).ravel(), x.ravel().astype(np.uint32))
+    model_bits = -np.log2((chi.astype(np.float64) - clo) / m.T).sum()
+    assert abs(model_bits - ideal_bits) <= 0.005 * ideal_bits
+    assert len(bits) * 8 >= model_bits  # no code beats its model
+
+
+def _gaussian_bf16(n, sigma, seed):
+    rng = np.random.default_rng(seed)
+    # predictor means on the bf16 grid inside [1.375, 1.625]; bin width there is 2^-7
+    mu16 = rng.integers(0x3FB0, 0x3FD0, n).astype(np.uint16)
+    mu = (mu16.astype(np.uint32) << 16).view(np.float32)
+    import torch
+    xf = mu.astype(np.float64) + sigma * rng.standard_normal(n)
+    x16 = torch.from_numpy(xf.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return x16, mu16, mu
+
+
+def test_closed_form_rate_pure_gaussian():
+    """With a single Gaussian of the calibrated sigma and bins of width D << sigma,
+    the rate is 1/2 log2(2 pi e sigma^2 / D^2) bits ('Speculative KV coding', what
+    q should look like: 1/2 log(2 pi e sigma^2) per scalar, in nats for a density),
+    plus log2(T / (T - N)) for the one-count floor."""
+    delta, sigma, n = 2.0 ** -7, 8 * 2.0 ** -7, 1_000_000
+    x16, mu16, mu = _gaussian_bf16(n, sigma, 9)
+    m = R.Model(0, None, w_narrow=1.0, w_wide=0.0, MG=(1 << 24) - 65536, Mp=0)
+    s = R.scale(np.full(n, sigma, np.float32))
+    clo, chi = m.cum_pair(mu, s, x16.astype(np.uint32))
+    rate = -np.log2((chi.astype(np.float64) - clo) / m.T).mean()
+    closed = 0.5 * math.log2(2 * math.pi * math.e * sigma ** 2 / delta ** 2) + math.log2(m.T / (m.T - m.N))
+    assert abs(rate - closed) < 0.01, (rate, closed)
+    # the default mixture pays at most -log2(0.95) for its spare components
+    md = R.Model(0)
+    clo, chi = md.cum_pair(mu, s, x16.astype(np.uint32))
+    rate_d = -np.log2((chi.astype(np.float64) - clo) / md.T).mean()
+    assert closed - 0.01 <= rate_d <= closed - math.log2(0.95) + 0.01
+
+
+def test_decoder_flags_corruption():
+    w = synth.WORKLOADS["tiny_bf16"]
+    sigma, hist = _calibrate(w)
+    x, mu = _cache(w)
+    m = R.Model(0, hist)
+    sh = _shape(w)
+    bits, offs = m.encode(sh, x, mu, sigma)
+    # header length that does not add up to the chunk
+    bad = bits.copy()
+    bad[0] ^= 1
+    _, st = m.decode(sh, bad, offs, mu, sigma)
+    assert st == R.ERR_CORRUPT
+    # zero-length substream
+    bad = bits.copy()
+    bad[2:4] = 0
+    _, st = m.decode(sh, bad, offs, mu, sigma)
+    assert st == R.ERR_CORRUPT
+    # flipped payload bytes: either flagged or decoded to something else, never silently right
+    rng = np.random.default_rng(10)
+    flagged = 0
+    for _ in range(20):
+        bad = bits.copy()
+        i = int(rng.integers(128, int(offs[1])))
+        bad[i] ^= 0xFF
+        out, st = m.decode(sh, bad, offs, mu, sigma)
+        assert st == R.ERR_CORRUPT or not np.array_equal(out, x)
+        flagged += st == R.ERR_CORRUPT
+    assert flagged > 0
+
+
+def test_chunk_api_matches_whole_cache():
+    w = synth.WORKLOADS["qwen3_0.6b_bf16"].with_tokens(600, layers=2)
+    sigma, hist = _calibrate(w)
+    x, mu = _cache(w)
+    m = R.Model(0, hist)
+    sh = _shape(w)
+    bits, offs = m.encode(sh, x, mu, sigma)
+    ntb = 3
+    xf, mf = x.reshape(-1), mu.reshape(-1)
+    for c in [0, 1, 2, 17, 95]:
+        row, blk = divmod(c, ntb)
+        base = row * w.tokens * w.head_dim + blk * 256 * w.head_dim
+        got = m.encode_chunk(sh, c, xf[base:], mf[base:], sigma[row * w.head_dim:])
+        np.testing.assert_array_equal(got, bits[int(offs[c]):int(offs[c + 1])])
+        out = np.zeros(256 * w.head_dim, np.uint16)
+        st = m.decode_chunk(sh, c, got, mf[base:], sigma[row * w.head_dim:], out)
+        n = min(256, w.tokens - 256 * blk) * w.head_dim
+        assert st == R.OK and np.array_equal(out[:n], xf[base:base + n])

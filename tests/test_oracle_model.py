@@ -1,0 +1,277 @@
+"""Pins for the oracle's frequency model (no GPU).
+
+Each test checks the oracle against something other than itself: the exact
+mixture CDF from scipy's ndtr, torch's round-to-nearest-even conversions,
+closed forms, and brute-force invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import ndtr
+
+from oracle import skvref as R
+
+FMTS = [R.SYM_BF16, R.SYM_E4M3]
+
+
+def exact_mix(z, w_narrow=0.95, w_wide=0.03):
+    z = np.asarray(z, dtype=np.float64)
+    return (w_narrow * ndtr(z) + w_wide * ndtr(z / 3.0)) / (w_narrow + w_wide)
+
+
+# ---------------------------------------------------------------- knots
+@pytest.mark.parametrize("fmt", FMTS)
+def test_knots_are_correctly_rounded_mixture_cdf(fmt):
+    """V_j = RN32(MG * G(j/64)), G the 0.95/0.03 Gaussian pair of the mixture
+    ("Speculative KV coding", early results), with G taken from scipy's ndtr."""
+    m = R.Model(fmt)
+    K, D = m.knots()
+    j = np.arange(0, 1024)
+    exact = m.MG * exact_mix(j / 64.0)
+    V = K[1024:2048].astype(np.float64)
+    ulp = np.spacing(np.abs(V).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(V - exact) <= 0.5 * ulp + 1e-9 * m.MG)
+    # every knot is far from an fp32 rounding boundary, so any accurate erfc rounds the same way
+    frac = (exact - V) / ulp
+    margin = 0.5 - np.abs(frac)
+    assert margin.min() > 1e-6, f"knot {np.argmin(margin)} is ambiguous: margin {margin.min()}"
+    assert K[2048] == m.MG
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_knot_table_structure(fmt):
+    m = R.Model(fmt)
+    K, D = m.knots()
+    Kd = K.astype(np.float64)
+    assert K[1024] == m.MG / 2 and K[0] == 0.0 and K[2048] == m.MG
+    # K_{-j} = MG - K_j exactly
+    np.testing.assert_array_equal(Kd[:1024][::-1], m.MG - Kd[1025:])
+    # D is the exact difference and non-negative; the top knot has D = 0
+    np.testing.assert_array_equal(D[:-1].astype(np.float64), Kd[1:] - Kd[:-1])
+    assert D[-1] == 0.0 and np.all(D >= 0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_cg_monotone_and_saturating(fmt):
+    m = R.Model(fmt)
+    rng = np.random.default_rng(1)
+    u = np.concatenate([
+        rng.uniform(-1100, 1100, 2_000_000),
+        rng.uniform(-2, 2, 500_000),
+        np.ldexp(rng.uniform(-1, 1, 200_000), rng.integers(-149, 10, 200_000)),
+        np.arange(-1025, 1026, 0.25),
+        [0.0, -0.0, np.inf, -np.inf, 1e30, -1e30, 1024.0, -1024.0, 1023.9999, -1023.9999],
+    ]).astype(np.float32)
+    u = np.sort(u)
+    cg = m.cg(u).astype(np.int64)
+    assert np.all(np.diff(cg) >= 0)
+    assert m.cg(np.array([-np.inf], np.float32))[0] == 0
+    assert m.cg(np.array([np.inf], np.float32))[0] == m.MG
+    assert m.cg(np.array([0.0], np.float32))[0] == m.MG // 2
+    assert m.cg(np.array([-0.0], np.float32))[0] == m.MG // 2
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_cg_within_interpolation_bound_of_exact(fmt):
+    """Linear interpolation between knots h = 1/64 apart is within h^2/8 max|G''|
+    of the exact mixture CDF; knot rounding adds 1/2 count and the floor 1."""
+    m = R.Model(fmt)
+    rng = np.random.default_rng(2)
+    u = rng.uniform(-1024, 1024, 1_000_000).astype(np.float32)
+    cg = m.cg(u).astype(np.float64)
+    exact = m.MG * exact_mix(u.astype(np.float64) / 64.0)
+    gpp_max = (0.95 * math.exp(-0.5) / math.sqrt(2 * math.pi) + 0.03 / 9 * math.exp(-0.5) / math.sqrt(2 * math.pi)) / 0.98
+    bound = m.MG * (1 / 64) ** 2 / 8 * gpp_max + 0.5 + 1.0
+    err = np.abs(cg - exact)
+    assert err.max() <= bound, (err.max(), bound)
+    # and clearly finer than that on average (catches a wrong segment index)
+    assert err.mean() < 0.5 * bound
+
+
+# ---------------------------------------------------------------- symbols and bins
+def _bf16_values(b):
+    return (np.asarray(b, np.uint32) << 16).astype(np.uint32).view(np.float32)
+
+
+def test_rank_is_value_order_bf16():
+    b = np.arange(65536, dtype=np.uint32)
+    ranks = np.array([R.rank(0, int(v)) for v in b])
+    assert sorted(ranks.tolist()) == list(range(65536))
+    assert all(R.unrank(0, int(R.rank(0, int(v)))) == v for v in b[::97])
+    order = np.argsort(ranks)
+    vals = _bf16_values(b[order]).astype(np.float64)
+    finite = ~np.isnan(vals)
+    assert np.all(np.isnan(vals[:127])) and np.all(np.isnan(vals[-127:]))
+    v = vals[finite]
+    assert np.all(np.diff(v) >= 0)  # -0 and +0 compare equal, in that order
+    assert np.signbit(vals[32767]) and not np.signbit(vals[32768])
+
+
+def test_rank_is_value_order_e4m3():
+    b = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(b).view(torch.float8_e4m3fn).float().numpy()
+    ranks = np.array([R.rank(1, int(v)) for v in b])
+    assert sorted(ranks.tolist()) == list(range(256))
+    order = np.argsort(ranks)
+    sv = vals[order]
+    assert np.isnan(sv[0]) and np.isnan(sv[-1])
+    assert np.all(np.diff(sv[1:-1]) >= 0)
+    for v in range(256):
+        assert R.value(1, v) == vals[v] or (np.isnan(vals[v]) and np.isnan(R.value(1, v)))
+
+
+def test_bf16_bins_are_rne_preimages():
+    """Points inside each bin round (torch fp32 -> bf16, RNE) to the symbol;
+    the fp32 neighbours just outside round to the adjacent symbols."""
+    b = np.arange(65536, dtype=np.uint32)
+    lo, hi = R.bins(0, b)
+    m = b & 0x7FFF
+    fin = (m >= 1) & (m <= 0x7F7F)
+    bb, lo_, hi_ = b[fin], lo[fin], hi[fin]
+    to_bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    inner_lo = np.nextafter(lo_, np.float32(np.inf))
+    inner_hi = np.nextafter(hi_, np.float32(-np.inf))
+    np.testing.assert_array_equal(to_bf(inner_lo), bb)
+    np.testing.assert_array_equal(to_bf(inner_hi), bb)
+    below = np.nextafter(lo_, np.float32(-np.inf))
+    above = np.nextafter(hi_, np.float32(np.inf))
+    rank = np.array([R.rank(0, int(v)) for v in bb])
+    rb = np.array([R.rank(0, int(v)) for v in to_bf(below)])
+    ra = np.array([R.rank(0, int(v)) for v in to_bf(above)])
+    np.testing.assert_array_equal(rb, rank - 1)
+    np.testing.assert_array_equal(ra, rank + 1)
+    # the edge itself is a tie and goes to the even mantissa
+    at_lo = to_bf(lo_)
+    even = (bb & 1) == 0
+    np.testing.assert_array_equal(at_lo[even], bb[even])
+    # specials: zeros, infinities, NaNs
+    assert R.bins(0, [0x0000]) == (np.float32(0.0), np.float32(2.0 ** -134))
+    lo0, hi0 = R.bins(0, [0x8000])
+    assert lo0[0] == -(2.0 ** -134) and hi0[0] == 0.0
+    lo_inf, hi_inf = R.bins(0, [0x7F80])
+    assert to_bf(np.nextafter(lo_inf, np.float32(np.inf)))[0] == 0x7F80 and hi_inf[0] == np.inf
+    assert R.bins(0, [0x7FC0])[0][0] == np.inf and R.bins(0, [0xFFC0])[1][0] == -np.inf
+
+
+def test_e4m3_bins_are_saturating_rne_preimages():
+    b = np.arange(256, dtype=np.uint32)
+    lo, hi = R.bins(1, b)
+
+    def to_e4(a):
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).clamp(-448, 448)
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    for v in range(256):
+        if (v & 0x7F) == 0x7F:
+            assert (lo[v], hi[v]) == ((np.inf, np.inf) if v < 128 else (-np.inf, -np.inf))
+            continue
+        pts = [np.nextafter(lo[v], np.float32(np.inf)), np.nextafter(hi[v], np.float32(-np.inf))]
+        pts = [p for p in pts if np.isfinite(p)]
+        if np.isinf(hi[v]):
+            pts.append(np.float32(1e30))
+        if np.isinf(lo[v]):
+            pts.append(np.float32(-1e30))
+        got = to_e4(np.array(pts, np.float32))
+        want = v if (v & 0x7F) else None
+        if want is not None:
+            assert np.all(got == v), (v, pts, got)
+        else:  # zeros: the sign of a rounded tiny value follows the value
+            assert np.all((got & 0x7F) == 0)
+    # interval ends meet in rank order
+    order = np.argsort([R.rank(1, v) for v in range(256)])
+    np.testing.assert_array_equal(hi[order][:-1], lo[order][1:])
+    assert lo[0x7E] == 432.0 and hi[0x7E] == np.inf and lo[0x01] == 2.0 ** -10
+
+
+def test_bf16_bin_ends_meet_in_rank_order():
+    b = np.array([R.unrank(0, k) for k in range(65536)], dtype=np.uint32)
+    lo, hi = R.bins(0, b)
+    np.testing.assert_array_equal(hi[:-1], lo[1:])
+    assert lo[0] == -np.inf and hi[-1] == np.inf
+
+
+# ---------------------------------------------------------------- p_hat table
+@pytest.mark.parametrize("fmt", FMTS)
+def test_ptable_uniform_closed_form(fmt):
+    m = R.Model(fmt)
+    A = m.ptable().astype(np.int64)
+    k = np.arange(m.N + 1, dtype=np.int64)
+    np.testing.assert_array_equal(A, k + (m.Mp * k) // m.N)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_ptable_tracks_smoothed_histogram(fmt):
+    rng = np.random.default_rng(3)
+    N = 65536 if fmt == 0 else 256
+    hist = rng.zipf(1.5, N).astype(np.uint64) * rng.integers(0, 2, N).astype(np.uint64)
+    m = R.Model(fmt, hist)
+    A = m.ptable().astype(np.int64)
+    order = np.array([R.unrank(fmt, k) for k in range(N)])
+    h = hist[order].astype(np.float64) + 1
+    dq = np.diff(A) - 1
+    expect = m.Mp * h / h.sum()
+    assert np.all(np.abs(dq - expect) < 1.0 + 1e-9)
+    assert A[0] == 0 and A[-1] == N + m.Mp
+
+
+# ---------------------------------------------------------------- the integer model
+def _samples(fmt, n, seed):
+    rng = np.random.default_rng(seed)
+    mu = np.concatenate([
+        rng.standard_normal(n // 2) * np.exp(rng.uniform(-8, 8, n // 2)),
+        np.ldexp(rng.uniform(-1, 1, n // 4), rng.integers(-140, -120, n // 4)),  # subnormal-ish
+        rng.uniform(-500, 500, n - n // 2 - n // 4 - 6),
+        [0.0, -0.0, np.nan, np.inf, -np.inf, 3e38],
+    ]).astype(np.float32)
+    sigma = np.exp(rng.uniform(-20, 20, mu.size)).astype(np.float32)
+    sigma[:: 7] = 0.0
+    sigma[1:: 11] = 2.0 ** -100
+    sigma[2:: 13] = 1e30
+    return mu, sigma
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_model_invariants_bruteforce(fmt):
+    """For every sample (mu, sigma): cum(0) = 0, cum(N) = T, every freq >= 1,
+    and the encoder's per-symbol pair equals the decoder's per-rank table."""
+    mu, sigma = _samples(fmt, 120 if fmt == 0 else 2000, 4)
+    hist = np.random.default_rng(5).integers(0, 1000, 65536 if fmt == 0 else 256).astype(np.uint64)
+    m = R.Model(fmt, hist)
+    b = np.array([R.unrank(fmt, k) for k in range(m.N)], dtype=np.uint32)
+    for i in range(mu.size):
+        cum = m.cum_table(mu[i], sigma[i]).astype(np.int64)
+        assert cum[0] == 0 and cum[-1] == m.T
+        assert np.all(np.diff(cum) >= 1)
+        s = R.scale(np.array([sigma[i]], np.float32))[0]
+        lo, hi = m.cum_pair(np.full(m.N, mu[i], np.float32), np.full(m.N, s, np.float32), b)
+        np.testing.assert_array_equal(lo, cum[:-1])
+        np.testing.assert_array_equal(hi, cum[1:])
+
+
+def test_scale_is_correctly_rounded():
+    rng = np.random.default_rng(6)
+    sigma = np.exp(rng.uniform(-60, 60, 200_000)).astype(np.float32)
+    s = R.scale(sigma)
+    from fractions import Fraction
+    for sg, sc in list(zip(sigma, s))[:2000]:
+        exact = Fraction(64) / Fraction(float(sg))
+        lo = Fraction(float(np.nextafter(sc, np.float32(0))))
+        hi = Fraction(float(np.nextafter(sc, np.float32(np.inf))))
+        c = Fraction(float(sc))
+        assert abs(exact - c) <= min(abs(exact - lo), abs(exact - hi))
+    assert R.scale(np.array([0.0], np.float32))[0] == np.float32(64.0 * 2.0 ** 100)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_pure_noise_predictor_costs_full_width(fmt):
+    """A predictor that carries no information costs the full symbol width
+    ("Speculative KV coding", what predicts the KV cache: close to 16 bits).
+    With the Gaussian budget set to 0 and an empty histogram every symbol
+    gets exactly 256 counts: 16 bits for bf16, 8 for e4m3."""
+    N = 65536 if fmt == 0 else 256
+    T = 1 << (24 if fmt == 0 else 16)
+    m = R.Model(fmt, None, MG=0, Mp=T - N)
+    cum = m.cum_table(0.3, 0.01).astype(np.int64)
+    assert np.all(np.diff(cum) == T // N)
