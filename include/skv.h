@@ -1,0 +1,174 @@
+/*
+ * skv.h -- C ABI of libskv, the MI355X (gfx950) speculative-KV-coding library.
+ *
+ * Speculative KV coding compresses a model's KV cache losslessly: a cheap
+ * predictor gives every cache scalar x a mean mu, a calibrated per-(kv, head,
+ * channel) sigma gives its spread, and an arithmetic coder spends about
+ * -log2 q(x) bits per scalar under the model
+ *     q = 0.95 N(mu, sigma^2) + 0.03 N(mu, (3 sigma)^2) + 0.02 p_hat,
+ * p_hat being the empirical symbol distribution, integrated over each
+ * symbol's bf16 or FP8-e4m3 bin.  Pages: "Speculative KV coding: lossless KV
+ * cache compression up to ~4x", sections "q 应是什么样的" (what q should look
+ * like), "什么能预测 KV 缓存" (what predicts the KV cache: the coder maps
+ * (KV_full, mu, sigma) to bits and (bits, mu, sigma) back), "早期结果" (early
+ * results: the mixture, sigma per (kv, head, channel)), "原生 FP8 KV 缓存"
+ * (native FP8 cache: bin-integrated model over e4m3 symbols).
+ *
+ * The integer model, the range coder and the stream layout (chunks of one
+ * (layer, kv, head) row x 256 tokens, 64 interleaved lane substreams, a u16
+ * length header, u64 chunk offsets) are specified in the design notes that
+ * ship with the library; the encoder output is a deterministic function of the
+ * inputs, byte for byte.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are device (HBM) pointers on the current HIP
+ *     device; (host) pointers are host memory.  The caller owns every buffer.
+ *     The library allocates no device memory: scratch comes from `workspace`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls validate their arguments on the host, then enqueue kernels on the
+ *     stream and return without synchronising.
+ *   - The return value reports synchronous errors (bad arguments, launch
+ *     failures).  Errors that depend on the data are written by the kernels to
+ *     `*status` (device int32, cleared by the call itself); read it after the
+ *     stream has run.  When *status != SKV_OK the outputs are unspecified but
+ *     every kernel stays inside the buffers described here.
+ *   - Calls are stateless; concurrent calls must use distinct workspaces.
+ *
+ * Cache layout (x, mu, x_out): [layers][2 (K=0, V=1)][kv_heads][tokens][head_dim],
+ * contiguous, 16-byte aligned.  head_dim must be a multiple of 8 that divides
+ * 512 (8 .. 512; Qwen3 uses 128).  Symbols are raw bit patterns.
+ */
+#ifndef SKV_H
+#define SKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum skv_status {
+  SKV_OK = 0,
+  SKV_ERR_ARG = 1,          /* bad argument (null pointer, bad shape, non-finite or negative sigma) */
+  SKV_ERR_UNSUPPORTED = 2,  /* head_dim not a multiple of 8 dividing 512 */
+  SKV_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
+  SKV_ERR_CAPACITY = 4,     /* the compressed stream does not fit bits_cap */
+  SKV_ERR_CORRUPT = 5,      /* the stream does not decode consistently */
+  SKV_ERR_TABLE = 6         /* histogram total too large for the p_hat table (Mp * total >= 2^64) */
+};
+
+enum skv_sym_fmt { SKV_SYM_BF16 = 0, SKV_SYM_E4M3 = 1 };
+enum skv_mu_fmt { SKV_MU_BF16 = 0, SKV_MU_F32 = 1 };
+
+typedef struct skv_shape {
+  int64_t layers;    /* >= 1 */
+  int64_t kv_heads;  /* >= 1 */
+  int64_t tokens;    /* >= 1; the last 256-token chunk of a row may be shorter */
+  int64_t head_dim;  /* multiple of 8 dividing 512 */
+  int32_t sym_fmt;   /* enum skv_sym_fmt: symbols are bf16 (uint16 patterns) or e4m3 (uint8 patterns) */
+  int32_t mu_fmt;    /* enum skv_mu_fmt: predictor means are bf16 (uint16 patterns) or fp32 */
+} skv_shape;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *skv_status_string(int status);
+
+/* ---------------------------------------------------------------- sizes (host only) */
+
+/* Number of chunks: layers * 2 * kv_heads * ceil(tokens / 256).  Chunk ids run
+ * over (layer, kv, head) rows, then 256-token blocks.  Returns SKV_ERR_ARG /
+ * SKV_ERR_UNSUPPORTED for a bad shape. */
+int skv_num_chunks(const skv_shape *shape, int64_t *n_chunks);
+
+/* Largest possible encoded size in bytes: n_chunks * (128 + 64) + 3 * n_scalars
+ * (a frequency of 1 in 2^24 costs at most 3 bytes; one flush byte per lane). */
+int skv_encode_bound(const skv_shape *shape, size_t *bytes);
+
+/* Device workspace needed by skv_encode and skv_decode for this shape. */
+int skv_workspace_size(const skv_shape *shape, size_t *bytes);
+
+/* Device workspace (calibration state) needed by the calibration calls: per
+ * channel an fp64 sum of squares and a u64 count, plus the u64 histogram. */
+int skv_calib_state_size(const skv_shape *shape, size_t *bytes);
+
+/* ---------------------------------------------------------------- calibration */
+/*
+ * sigma^2 = E[(KV_full - mu)^2] minimises the expected code length ("q 应是
+ * 什么样的"); it is measured per (layer, kv, head, channel) on a small
+ * calibration set and frozen ("同一模型的优化版本", "早期结果"), and p_hat is
+ * the calibration set's symbol histogram ("早期结果").
+ *
+ * Per channel c, over the calibration scalars with a finite symbol value v:
+ *   S_c += RN64(r * r), r = RN64(v - mu'), n_c += 1, in call order then token
+ *   order (mu' = mu in fp32, or 0 when mu is not finite);
+ *   sigma_c = RN32(sqrt(RN64(S_c / n_c))), or 1.0 when n_c = 0.
+ * hist[b] counts every symbol pattern b (NaN patterns included).
+ * The result is deterministic: sums are fp64 in a fixed order and the
+ * histogram uses integer atomics only.
+ */
+
+/* Clear a calibration state of skv_calib_state_size(shape) bytes (device). */
+int skv_calib_reset(void *state, const skv_shape *shape, void *stream);
+
+/* Add one batch of calibration sequences: x and mu (device) laid out like a
+ * cache of shape seq_shape.  seq_shape must match the state's shape in
+ * layers, kv_heads, head_dim and formats; tokens may differ per call. */
+int skv_calib_accumulate(void *state, const skv_shape *seq_shape, const void *x, const void *mu,
+                         void *stream);
+
+/* sigma (device, fp32 [layers][2][kv_heads][head_dim]) and hist (device, u64
+ * [65536] for bf16, [256] for e4m3, indexed by bit pattern, raw counts) from
+ * the state.  The state is left unchanged. */
+int skv_calib_finalize(const void *state, const skv_shape *shape, float *sigma, uint64_t *hist,
+                       void *stream);
+
+/* Convenience: reset, accumulate n_seq sequences stored back to back (each of
+ * shape seq_shape), finalize.  state: skv_calib_state_size(seq_shape) bytes. */
+int skv_calibrate(const skv_shape *seq_shape, int64_t n_seq, const void *x, const void *mu,
+                  float *sigma, uint64_t *hist, void *state, void *stream);
+
+/* ---------------------------------------------------------------- encode / decode */
+
+/*
+ * Encode a cache.
+ *   x       (device) symbols, cache layout, bf16 or e4m3 patterns
+ *   mu      (device) predictor means, cache layout, bf16 patterns or fp32
+ *   sigma   (device) fp32 [layers][2][kv_heads][head_dim], finite and >= 0
+ *           (sigma below 2^-100 is treated as 2^-100)
+ *   hist    (device) u64 symbol histogram as produced by skv_calib_finalize
+ *   bits    (device) output stream, bits_cap bytes (>= skv_encode_bound
+ *           guarantees success); 16-byte aligned
+ *   offsets (device) u64 [n_chunks + 1]: chunk c is bits[offsets[c], offsets[c+1]);
+ *           offsets[n_chunks] is the stream's total size
+ *   workspace (device) skv_workspace_size(shape) bytes
+ *   status  (device) int32: SKV_OK, SKV_ERR_CAPACITY (stream larger than
+ *           bits_cap; offsets are still valid), SKV_ERR_ARG (bad sigma),
+ *           SKV_ERR_TABLE (histogram too large)
+ */
+int skv_encode(const skv_shape *shape, const void *x, const void *mu, const float *sigma,
+               const uint64_t *hist, uint8_t *bits, size_t bits_cap, uint64_t *offsets,
+               void *workspace, size_t workspace_bytes, int32_t *status, void *stream);
+
+/*
+ * Decode a cache encoded by skv_encode with the same shape, mu, sigma and hist
+ * (the model is not stored in the stream: both ends rebuild it, "什么能预测 KV
+ * 缓存").
+ *   bits     (device) the stream, bits_bytes readable bytes; no read leaves
+ *            [bits, bits + bits_bytes) whatever offsets and headers say
+ *   offsets  (device) u64 [n_chunks + 1] (a chunk outside bits_bytes, or with
+ *            offsets[c+1] < offsets[c], decodes as corrupt)
+ *   x_out    (device) decoded symbols, cache layout
+ *   status   (device) int32: SKV_OK or SKV_ERR_CORRUPT (header lengths that do
+ *            not add up, a quotient outside the frequency total, or a substream
+ *            whose length disagrees with what its symbols consumed), or the
+ *            model errors of skv_encode
+ */
+int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bits_bytes,
+               const uint64_t *offsets, const void *mu, const float *sigma, const uint64_t *hist,
+               void *x_out, void *workspace, size_t workspace_bytes, int32_t *status, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKV_H */

@@ -1,0 +1,206 @@
+// skv_api.hip -- the C ABI of libskv: argument checks, workspace layout and
+// kernel launches on the caller's stream.  Declarations and contracts: skv.h.
+#include <math.h>
+
+#include "skv_internal.hpp"
+
+using namespace skv;
+
+extern "C" const char *skv_status_string(int status) {
+  switch (status) {
+    case SKV_OK: return "ok";
+    case SKV_ERR_ARG: return "invalid argument";
+    case SKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be a multiple of 8 dividing 512)";
+    case SKV_ERR_HIP: return "HIP runtime error";
+    case SKV_ERR_CAPACITY: return "compressed stream exceeds the output capacity";
+    case SKV_ERR_CORRUPT: return "corrupt stream";
+    case SKV_ERR_TABLE: return "histogram too large for the p_hat table";
+    default: return "unknown status";
+  }
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// shape checks and derived geometry; returns SKV_OK or an error
+int make_geo(const skv_shape *sh, Geo &g) {
+  if (!sh) return SKV_ERR_ARG;
+  if (sh->layers < 1 || sh->kv_heads < 1 || sh->tokens < 1 || sh->head_dim < 1) return SKV_ERR_ARG;
+  if (sh->sym_fmt != SKV_SYM_BF16 && sh->sym_fmt != SKV_SYM_E4M3) return SKV_ERR_ARG;
+  if (sh->mu_fmt != SKV_MU_BF16 && sh->mu_fmt != SKV_MU_F32) return SKV_ERR_ARG;
+  if (sh->head_dim % kGroup != 0 || (kGroup * kLanes) % sh->head_dim != 0) return SKV_ERR_UNSUPPORTED;
+  if (sh->layers > (1 << 20) || sh->kv_heads > (1 << 16) || sh->tokens > (int64_t(1) << 32)) return SKV_ERR_ARG;
+  g.layers = sh->layers;
+  g.heads = sh->kv_heads;
+  g.tokens = sh->tokens;
+  g.D = sh->head_dim;
+  g.ntb = (sh->tokens + kChunkTokens - 1) / kChunkTokens;
+  g.rows = sh->layers * 2 * sh->kv_heads;
+  g.n_chunks = g.rows * g.ntb;
+  g.sym_fmt = sh->sym_fmt;
+  g.mu_fmt = sh->mu_fmt;
+  g.N = sh->sym_fmt == SKV_SYM_BF16 ? 65536u : 256u;
+  g.log2T = sh->sym_fmt == SKV_SYM_BF16 ? 24u : 16u;
+  // one count per symbol; the rest split 0.98 : 0.02 between the Gaussian
+  // pair and p_hat, the mixture's weights ("Speculative KV coding", "早期结果")
+  uint32_t budget = (1u << g.log2T) - g.N;
+  g.MG = (uint32_t)llround(0.98 * (double)budget);
+  g.Mp = budget - g.MG;
+  // most bytes a lane can emit: 3 per symbol (4 * head_dim symbols) + 1
+  g.lane_cap = (uint32_t)((3 * 4 * g.D + 1 + 3) / 4 * 4);
+  return SKV_OK;
+}
+
+struct Layout {
+  size_t knots, ptab, etab, scale, lens, sizes, scratch, total;
+};
+
+Layout layout(const Geo &g) {
+  Layout L;
+  size_t o = 0;
+  L.knots = o; o = align_up(o + sizeof(float2) * kNKnot);
+  L.ptab = o;  o = align_up(o + sizeof(uint32_t) * (g.N + 1));
+  L.etab = o;  o = align_up(o + sizeof(float2) * 256);
+  L.scale = o; o = align_up(o + sizeof(float) * (size_t)(g.rows * g.D));
+  L.lens = o;  o = align_up(o + sizeof(uint32_t) * (size_t)g.n_chunks * kLanes);
+  L.sizes = o; o = align_up(o + sizeof(uint64_t) * (size_t)g.n_chunks);
+  L.scratch = o; o = align_up(o + (size_t)g.n_chunks * kLanes * g.lane_cap);
+  L.total = o;
+  return L;
+}
+
+Workspace carve(const Geo &g, void *base) {
+  Layout L = layout(g);
+  uint8_t *b = static_cast<uint8_t *>(base);
+  Workspace w;
+  w.knots = reinterpret_cast<float2 *>(b + L.knots);
+  w.ptab = reinterpret_cast<uint32_t *>(b + L.ptab);
+  w.etab = reinterpret_cast<float2 *>(b + L.etab);
+  w.scale = reinterpret_cast<float *>(b + L.scale);
+  w.lens = reinterpret_cast<uint32_t *>(b + L.lens);
+  w.sizes = reinterpret_cast<uint64_t *>(b + L.sizes);
+  w.scratch = b + L.scratch;
+  return w;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" int skv_num_chunks(const skv_shape *shape, int64_t *n_chunks) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!n_chunks) return SKV_ERR_ARG;
+  *n_chunks = g.n_chunks;
+  return SKV_OK;
+}
+
+extern "C" int skv_encode_bound(const skv_shape *shape, size_t *bytes) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!bytes) return SKV_ERR_ARG;
+  size_t nsc = (size_t)(g.rows * g.tokens * g.D);
+  *bytes = (size_t)g.n_chunks * (kHeaderBytes + kLanes) + 3 * nsc;
+  return SKV_OK;
+}
+
+extern "C" int skv_workspace_size(const skv_shape *shape, size_t *bytes) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!bytes) return SKV_ERR_ARG;
+  *bytes = layout(g).total;
+  return SKV_OK;
+}
+
+extern "C" int skv_calib_state_size(const skv_shape *shape, size_t *bytes) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!bytes) return SKV_ERR_ARG;
+  *bytes = sizeof(uint64_t) * (size_t)(2 * g.rows * g.D + g.N);
+  return SKV_OK;
+}
+
+extern "C" int skv_calib_reset(void *state, const skv_shape *shape, void *stream) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!state) return SKV_ERR_ARG;
+  return hip_status(launch_calib_reset(g, state, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int skv_calib_accumulate(void *state, const skv_shape *seq_shape, const void *x, const void *mu,
+                                    void *stream) {
+  Geo g;
+  int e = make_geo(seq_shape, g);
+  if (e != SKV_OK) return e;
+  if (!state || !x || !mu) return SKV_ERR_ARG;
+  return hip_status(launch_calib_accumulate(g, state, x, mu, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int skv_calib_finalize(const void *state, const skv_shape *shape, float *sigma, uint64_t *hist,
+                                  void *stream) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!state || !sigma || !hist) return SKV_ERR_ARG;
+  return hip_status(launch_calib_finalize(g, state, sigma, hist, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int skv_calibrate(const skv_shape *seq_shape, int64_t n_seq, const void *x, const void *mu,
+                             float *sigma, uint64_t *hist, void *state, void *stream) {
+  Geo g;
+  int e = make_geo(seq_shape, g);
+  if (e != SKV_OK) return e;
+  if (n_seq < 0 || !x || !mu || !sigma || !hist || !state) return SKV_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((e = hip_status(launch_calib_reset(g, state, st))) != SKV_OK) return e;
+  const size_t nsc = (size_t)(g.rows * g.tokens * g.D);
+  const size_t xb = nsc * (g.sym_fmt == SKV_SYM_BF16 ? 2 : 1);
+  const size_t mb = nsc * (g.mu_fmt == SKV_MU_BF16 ? 2 : 4);
+  for (int64_t j = 0; j < n_seq; ++j) {
+    e = hip_status(launch_calib_accumulate(g, state, static_cast<const uint8_t *>(x) + j * xb,
+                                           static_cast<const uint8_t *>(mu) + j * mb, st));
+    if (e != SKV_OK) return e;
+  }
+  return hip_status(launch_calib_finalize(g, state, sigma, hist, st));
+}
+
+extern "C" int skv_encode(const skv_shape *shape, const void *x, const void *mu, const float *sigma,
+                          const uint64_t *hist, uint8_t *bits, size_t bits_cap, uint64_t *offsets, void *workspace,
+                          size_t workspace_bytes, int32_t *status, void *stream) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!x || !mu || !sigma || !hist || !bits || !offsets || !workspace || !status) return SKV_ERR_ARG;
+  if (!aligned16(x) || !aligned16(mu) || !aligned16(workspace)) return SKV_ERR_ARG;
+  if (workspace_bytes < layout(g).total) return SKV_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Workspace ws = carve(g, workspace);
+  if ((e = hip_status(launch_clear_status(status, st))) != SKV_OK) return e;
+  if ((e = hip_status(launch_model(g, sigma, hist, ws, status, st))) != SKV_OK) return e;
+  return hip_status(launch_encode(g, x, mu, ws, bits, bits_cap, offsets, status, st));
+}
+
+extern "C" int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bits_bytes, const uint64_t *offsets,
+                          const void *mu, const float *sigma, const uint64_t *hist, void *x_out, void *workspace,
+                          size_t workspace_bytes, int32_t *status, void *stream) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!bits || !offsets || !mu || !sigma || !hist || !x_out || !workspace || !status) return SKV_ERR_ARG;
+  if (!aligned16(mu) || !aligned16(x_out) || !aligned16(workspace)) return SKV_ERR_ARG;
+  if (workspace_bytes < layout(g).total) return SKV_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Workspace ws = carve(g, workspace);
+  if ((e = hip_status(launch_clear_status(status, st))) != SKV_OK) return e;
+  if ((e = hip_status(launch_model(g, sigma, hist, ws, status, st))) != SKV_OK) return e;
+  return hip_status(launch_decode(g, bits, bits_bytes, offsets, mu, ws, x_out, status, st));
+}

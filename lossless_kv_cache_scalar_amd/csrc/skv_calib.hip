@@ -1,0 +1,183 @@
+// skv_calib.hip -- calibration of sigma and p_hat on gfx950.
+//
+// sigma^2 = E[(KV_full - mu)^2] is the cost-minimising variance ("Speculative
+// KV coding", "q 应是什么样的"), measured per (layer, kv, head, channel) on a
+// small calibration set and frozen ("同一模型的优化版本", "早期结果"); p_hat is
+// the calibration symbol histogram ("早期结果").  Results are deterministic:
+// one thread owns a channel and sums its fp64 squares in token order, and the
+// histogram uses integer atomics only.
+//
+// State layout: S (fp64 [channels]) | n (u64 [channels]) | hist (u64 [N]).
+#include "skv_internal.hpp"
+
+namespace skv {
+
+struct CalState {
+  double *S;
+  uint64_t *n;
+  uint64_t *hist;
+};
+
+static CalState cal_state(const Geo &g, void *state) {
+  int64_t nch = g.rows * g.D;
+  CalState c;
+  c.S = static_cast<double *>(state);
+  c.n = reinterpret_cast<uint64_t *>(c.S + nch);
+  c.hist = c.n + nch;
+  return c;
+}
+
+__global__ void k_fill_u64(uint64_t *p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_calib_reset(const Geo &g, void *state, hipStream_t st) {
+  int64_t words = 2 * g.rows * g.D + g.N;  // S, n and hist are all 8-byte words
+  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+                     static_cast<uint64_t *>(state), words);
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ double e4m3_value(uint32_t b) {
+  uint32_t c = b & 0x7Fu;
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8u + m), (int)e - 10);
+  return (b & 0x80u) ? -v : v;
+}
+
+// One thread per channel: over the call's tokens in order, S += RN(r * r).
+template <int SYM, int MU>
+__global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, const void *__restrict__ mu,
+                                                    double *__restrict__ S, uint64_t *__restrict__ n, int64_t rows,
+                                                    int64_t tokens, int64_t D) {
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= rows * D) return;
+  const int64_t row = c / D, d = c % D;
+  double acc = S[c];
+  uint64_t cnt = n[c];
+  for (int64_t t = 0; t < tokens; ++t) {
+    const int64_t i = (row * tokens + t) * D + d;
+    double v;
+    bool fin;
+    if (SYM == SKV_SYM_BF16) {
+      float f = __uint_as_float((uint32_t)static_cast<const uint16_t *>(x)[i] << 16);
+      fin = __builtin_isfinite(f);
+      v = (double)f;
+    } else {
+      uint32_t b = static_cast<const uint8_t *>(x)[i];
+      fin = (b & 0x7Fu) != 0x7Fu;
+      v = fin ? e4m3_value(b) : 0.0;
+    }
+    if (!fin) continue;
+    float m = MU == SKV_MU_BF16 ? mu_from_bf16(static_cast<const uint16_t *>(mu)[i])
+                                : mu_from_f32(static_cast<const float *>(mu)[i]);
+    double r = v - (double)m;
+    double rr = r * r;
+    acc = acc + rr;
+    ++cnt;
+  }
+  S[c] = acc;
+  n[c] = cnt;
+}
+
+// Histogram: LDS counters for a window of 32768 bins, packed two 16-bit
+// counts per word; a block takes a tile of at most 65535 symbols so no count
+// can overflow, then adds its non-zero counts to the u64 histogram.
+constexpr int kHistWindow = 32768;
+constexpr int64_t kHistTile = 65535;
+
+template <int SYM>
+__global__ __launch_bounds__(1024) void k_calib_hist(const void *__restrict__ x, int64_t n, uint64_t *__restrict__ hist,
+                                                     uint32_t win0) {
+  __shared__ uint32_t cnt[kHistWindow / 2];
+  const uint32_t nbins = SYM == SKV_SYM_BF16 ? kHistWindow : 256;
+  for (uint32_t i = threadIdx.x; i < nbins / 2; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int64_t t0 = (int64_t)blockIdx.x * kHistTile;
+  const int64_t t1 = min<int64_t>(n, t0 + kHistTile);
+  for (int64_t i = t0 + threadIdx.x; i < t1; i += blockDim.x) {
+    uint32_t b = SYM == SKV_SYM_BF16 ? (uint32_t) static_cast<const uint16_t *>(x)[i]
+                                     : (uint32_t) static_cast<const uint8_t *>(x)[i];
+    uint32_t rel = b - win0;
+    if (rel < nbins) atomicAdd(&cnt[rel >> 1], 1u << (16 * (rel & 1u)));
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < nbins; i += blockDim.x) {
+    uint32_t v = (cnt[i >> 1] >> (16 * (i & 1u))) & 0xFFFFu;
+    if (v) atomicAdd(reinterpret_cast<unsigned long long *>(&hist[win0 + i]), (unsigned long long)v);
+  }
+}
+
+hipError_t launch_calib_accumulate(const Geo &g, void *state, const void *x, const void *mu, hipStream_t st) {
+  CalState cs = cal_state(g, state);
+  int64_t nch = g.rows * g.D;
+  dim3 grid((unsigned)((nch + 255) / 256)), blk(256);
+  if (g.sym_fmt == SKV_SYM_BF16) {
+    if (g.mu_fmt == SKV_MU_BF16)
+      hipLaunchKernelGGL((k_calib_sums<SKV_SYM_BF16, SKV_MU_BF16>), grid, blk, 0, st, x, mu, cs.S, cs.n, g.rows, g.tokens, g.D);
+    else
+      hipLaunchKernelGGL((k_calib_sums<SKV_SYM_BF16, SKV_MU_F32>), grid, blk, 0, st, x, mu, cs.S, cs.n, g.rows, g.tokens, g.D);
+  } else {
+    if (g.mu_fmt == SKV_MU_BF16)
+      hipLaunchKernelGGL((k_calib_sums<SKV_SYM_E4M3, SKV_MU_BF16>), grid, blk, 0, st, x, mu, cs.S, cs.n, g.rows, g.tokens, g.D);
+    else
+      hipLaunchKernelGGL((k_calib_sums<SKV_SYM_E4M3, SKV_MU_F32>), grid, blk, 0, st, x, mu, cs.S, cs.n, g.rows, g.tokens, g.D);
+  }
+  int64_t total = g.rows * g.tokens * g.D;
+  dim3 hgrid((unsigned)((total + kHistTile - 1) / kHistTile)), hblk(1024);
+  if (g.sym_fmt == SKV_SYM_BF16) {
+    for (uint32_t w = 0; w < 65536u; w += kHistWindow)
+      hipLaunchKernelGGL(k_calib_hist<SKV_SYM_BF16>, hgrid, hblk, 0, st, x, total, cs.hist, w);
+  } else {
+    hipLaunchKernelGGL(k_calib_hist<SKV_SYM_E4M3>, hgrid, hblk, 0, st, x, total, cs.hist, 0u);
+  }
+  return hipGetLastError();
+}
+
+// sigma = RN32(sqrt(q)), q = RN64(S / n): start from the fp64 square root and
+// settle the fp32 rounding by comparing q with the squares of the midpoints
+// between neighbouring fp32 values, which fp64 holds exactly (ties to even).
+__device__ float rn32_sqrt(double q) {
+  float s = (float)__builtin_sqrt(q);
+  for (int it = 0; it < 4; ++it) {
+    if (!__builtin_isfinite(s)) break;
+    uint32_t sb = __float_as_uint(s);
+    float up = __uint_as_float(sb + 1);
+    double mu = 0.5 * ((double)s + (double)up);
+    double mu2 = mu * mu;
+    if (mu2 < q || (mu2 == q && (sb & 1u))) {
+      s = up;
+      continue;
+    }
+    if (sb == 0) break;
+    float dn = __uint_as_float(sb - 1);
+    double md = 0.5 * ((double)s + (double)dn);
+    double md2 = md * md;
+    if (md2 > q || (md2 == q && (sb & 1u))) {
+      s = dn;
+      continue;
+    }
+    break;
+  }
+  return s;
+}
+
+__global__ void k_calib_finalize(const double *__restrict__ S, const uint64_t *__restrict__ n,
+                                 const uint64_t *__restrict__ hist_in, float *__restrict__ sigma,
+                                 uint64_t *__restrict__ hist_out, int64_t nch, int64_t N) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nch) sigma[i] = n[i] == 0 ? 1.0f : rn32_sqrt(S[i] / (double)n[i]);
+  if (i < N) hist_out[i] = hist_in[i];
+}
+
+hipError_t launch_calib_finalize(const Geo &g, const void *state, float *sigma, uint64_t *hist, hipStream_t st) {
+  CalState cs = cal_state(g, const_cast<void *>(state));
+  int64_t nch = g.rows * g.D;
+  int64_t m = nch > (int64_t)g.N ? nch : (int64_t)g.N;
+  hipLaunchKernelGGL(k_calib_finalize, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, cs.S, cs.n, cs.hist, sigma,
+                     hist, nch, (int64_t)g.N);
+  return hipGetLastError();
+}
+
+}  // namespace skv

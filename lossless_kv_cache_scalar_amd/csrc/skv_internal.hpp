@@ -1,0 +1,124 @@
+// skv_internal.hpp -- shared definitions of the HIP implementation (gfx950).
+//
+// The model and stream format implemented here (constants, bins, the knot
+// table of the Gaussian pair, the p_hat table, the range coder, chunks and
+// lanes) are those of speculative KV coding: q = 0.95 N(mu, sigma^2) +
+// 0.03 N(mu, (3 sigma)^2) + 0.02 p_hat integrated over each symbol's bin
+// ("Speculative KV coding", sections "q 应是什么样的", "早期结果",
+// "原生 FP8 KV 缓存"), made integer with a one-count floor per symbol and
+// coded by a 48-bit byte range coder in 64 lane substreams per chunk.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "skv.h"
+
+namespace skv {
+
+constexpr int kChunkTokens = 256;
+constexpr int kLanes = 64;        // one wavefront: one lane per substream
+constexpr int kGroup = 8;         // consecutive scalars a lane takes at a time
+constexpr int kKnotsPerUnit = 64; // knot spacing 1/64 in z
+constexpr int kUMax = 1024;       // knots cover |z| <= 16
+constexpr int kNKnot = 2 * kUMax + 1;
+constexpr int kHeaderBytes = 2 * kLanes;
+constexpr int kWavesPerBlock = 4;
+constexpr uint64_t kW48 = 0xFFFFFFFFFFFFull;
+constexpr uint64_t kTop40 = 1ull << 40;
+
+// Everything a kernel needs to know about the shape and the model constants.
+struct Geo {
+  int64_t layers, heads, tokens, D;
+  int64_t ntb;       // 256-token blocks per row
+  int64_t rows;      // layers * 2 * heads
+  int64_t n_chunks;
+  int sym_fmt, mu_fmt;
+  uint32_t N;        // alphabet: 65536 or 256
+  uint32_t log2T;    // 24 or 16
+  uint32_t MG, Mp;   // Gaussian-pair and p_hat budgets, MG + Mp = 2^log2T - N
+  uint32_t lane_cap; // encoder scratch bytes per lane (multiple of 4)
+};
+
+// ---- workspace layout (encode and decode share it) ----
+struct Workspace {
+  float2 *knots;      // kNKnot (K_j, K_{j+1} - K_j)
+  uint32_t *ptab;     // N + 1: A(k) = k + Qhat(k)
+  float2 *etab;       // 256 e4m3 bins (lo, hi), indexed by pattern
+  float *scale;       // per channel: RN32(64 / max(sigma, 2^-100))
+  uint32_t *lens;     // n_chunks * 64 substream lengths (encode)
+  uint64_t *sizes;    // n_chunks chunk sizes (encode)
+  uint8_t *scratch;   // n_chunks * 64 * lane_cap (encode)
+};
+
+// ---- symbol order ----
+__device__ __forceinline__ uint32_t rank_bf16(uint32_t b) { return b ^ ((b & 0x8000u) ? 0xFFFFu : 0x8000u); }
+__device__ __forceinline__ uint32_t unrank_bf16(uint32_t k) { return k ^ ((k & 0x8000u) ? 0x8000u : 0xFFFFu); }
+__device__ __forceinline__ uint32_t rank_e4m3(uint32_t b) { return b ^ ((b & 0x80u) ? 0xFFu : 0x80u); }
+__device__ __forceinline__ uint32_t unrank_e4m3(uint32_t k) { return k ^ ((k & 0x80u) ? 0x80u : 0xFFu); }
+
+// bf16 bin of pattern b: the fp32 values that round (nearest-even) to b.
+// Magnitude m in [1, 0x7F7F]: [m - half ulp, m + half ulp] in fp32 bit
+// arithmetic; +-0 meet at 0; +-inf reach +-inf; NaN bins are empty at +-inf.
+__device__ __forceinline__ void bf16_bin(uint32_t b, float &lo, float &hi) {
+  uint32_t m = b & 0x7FFFu;
+  uint32_t sh = m << 16;
+  uint32_t a = m == 0 ? 0u : sh - 0x8000u;
+  uint32_t c = sh + 0x8000u;
+  if (m >= 0x7F80u) {
+    c = 0x7F800000u;
+    if (m > 0x7F80u) a = 0x7F800000u;
+  }
+  uint32_t sgn = (b & 0x8000u) << 16;
+  lo = __uint_as_float(sgn ? (c | sgn) : a);
+  hi = __uint_as_float(sgn ? (a | sgn) : c);
+}
+
+__device__ __forceinline__ float bf16_lo_edge(uint32_t b) {
+  float lo, hi;
+  bf16_bin(b, lo, hi);
+  return lo;
+}
+
+// predictor mean in fp32; a non-finite mean reads as 0
+__device__ __forceinline__ float mu_from_bf16(uint32_t bits16) {
+  float f = __uint_as_float(bits16 << 16);
+  return __builtin_isfinite(f) ? f : 0.0f;
+}
+__device__ __forceinline__ float mu_from_f32(float f) { return __builtin_isfinite(f) ? f : 0.0f; }
+
+// knot coordinate u = RN(RN(e - mu) * s); the build turns contraction off
+__device__ __forceinline__ float u_of(float e, float mu, float s) {
+  float t = e - mu;
+  return t * s;
+}
+
+// Gaussian-pair CDF in counts: straight line between knots 1/64 apart in z.
+__device__ __forceinline__ uint32_t cg_eval(const float2 *__restrict__ kn, float u) {
+  float c = __builtin_fminf(__builtin_fmaxf(u, -(float)kUMax), (float)kUMax);
+  float fl = __builtin_floorf(c);
+  int i = (int)fl;
+  float f = c - fl;
+  float2 kd = kn[i + kUMax];
+  float y = __builtin_fmaf(f, kd.y, kd.x);
+  return (uint32_t)y;
+}
+
+__device__ __forceinline__ uint32_t bswap32(uint32_t v) { return __builtin_bswap32(v); }
+
+// first error wins
+__device__ __forceinline__ void set_status(int32_t *status, int32_t code) { atomicCAS(status, 0, code); }
+
+// ---- launchers (defined in the .hip files) ----
+hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, const Workspace &ws,
+                        int32_t *status, hipStream_t st);
+hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Workspace &ws, uint8_t *bits,
+                         uint64_t bits_cap, uint64_t *offsets, int32_t *status, hipStream_t st);
+hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes, const uint64_t *offsets, const void *mu,
+                         const Workspace &ws, void *x_out, int32_t *status, hipStream_t st);
+hipError_t launch_clear_status(int32_t *status, hipStream_t st);
+hipError_t launch_calib_reset(const Geo &g, void *state, hipStream_t st);
+hipError_t launch_calib_accumulate(const Geo &g, void *state, const void *x, const void *mu, hipStream_t st);
+hipError_t launch_calib_finalize(const Geo &g, const void *state, float *sigma, uint64_t *hist, hipStream_t st);
+
+}  // namespace skv

@@ -1,0 +1,156 @@
+// skv_model.hip -- per-call model build: knot table, p_hat table, e4m3 bins,
+// per-channel scales.  Small kernels; they run before every encode / decode.
+#include "skv_internal.hpp"
+
+namespace skv {
+
+// ---------------------------------------------------------------- knots
+// Gaussian pair of the mixture, normalised to its weight 0.98 ("Speculative KV
+// coding", "早期结果": 0.95 N(mu, sigma^2) + 0.03 N(mu, (3 sigma)^2)):
+//   G(z) = (0.95 Phi(z) + 0.03 Phi(z / 3)) / 0.98,  Phi(x) = erfc(-x / sqrt 2) / 2.
+// In counts at z = j / 64: V_j = RN32(MG G(j/64)) for 0 <= j < 1024, V_1024 = MG;
+// K_j = V_j (j >= 0), MG - V_{-j} (j < 0); the table holds (K_j, K_{j+1} - K_j).
+// fp64 erfc is accurate to a few ulp, far inside the distance of every knot's
+// exact value from an fp32 rounding boundary, so the rounding is the exact one.
+__global__ __launch_bounds__(1024) void k_knots(float2 *__restrict__ out, uint32_t MG) {
+  __shared__ float V[kUMax + 1];
+  __shared__ float K[kNKnot];
+  const double inv_sqrt2 = 0.70710678118654752440;
+  for (int j = threadIdx.x; j <= kUMax; j += blockDim.x) {
+    if (j == kUMax) {
+      V[j] = (float)MG;
+    } else {
+      double z = (double)j / (double)kKnotsPerUnit;
+      double p1 = 0.5 * erfc(-z * inv_sqrt2);
+      double p3 = 0.5 * erfc(-(z / 3.0) * inv_sqrt2);
+      double g = (0.95 * p1 + 0.03 * p3) / 0.98;
+      V[j] = (float)((double)MG * g);
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < kNKnot; j += blockDim.x) {
+    int jj = j - kUMax;
+    K[j] = jj >= 0 ? V[jj] : (float)MG - V[-jj];
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < kNKnot; j += blockDim.x) {
+    float d = j + 1 < kNKnot ? K[j + 1] - K[j] : 0.0f;
+    out[j] = make_float2(K[j], d);
+  }
+}
+
+// ---------------------------------------------------------------- p_hat table
+// p_hat: the calibration symbol histogram, +1 smoothed, in rank order
+// ("早期结果": the empirical bf16 symbol distribution).  H(0) = 0,
+// H(k+1) = H(k) + hist[unrank(k)] + 1, Qhat(k) = floor(Mp H(k) / H(N));
+// A(k) = k + Qhat(k) carries the one-count floor of every symbol.
+// One block of 1024 threads, each owning N / 1024 consecutive ranks (N = 256
+// uses the first 256 threads, one rank each).
+__global__ __launch_bounds__(1024) void k_ptable(const uint64_t *__restrict__ hist, uint32_t *__restrict__ A,
+                                                 uint32_t N, uint32_t Mp, int bf16, int32_t *status) {
+  __shared__ uint64_t part[1024];
+  __shared__ int bad;
+  const int t = threadIdx.x;
+  const uint32_t per = N >= 1024 ? N / 1024 : 1;
+  const uint32_t k0 = t * per;
+  const bool active = k0 < N;
+  uint64_t s = 0;
+  if (active)
+    for (uint32_t k = k0; k < k0 + per; ++k) {
+      uint32_t b = bf16 ? unrank_bf16(k) : unrank_e4m3(k);
+      s += hist[b] + 1;
+    }
+  part[t] = s;
+  if (t == 0) bad = 0;
+  __syncthreads();
+  // inclusive scan (Hillis-Steele) over the 1024 partial sums
+  for (int off = 1; off < 1024; off <<= 1) {
+    uint64_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  const uint64_t total = part[1023];
+  uint64_t H = part[t] - s;  // exclusive prefix
+  // Mp * H(N) must fit 64 bits; a histogram that large (or one whose counts
+  // wrapped) falls back to the uniform table so every frequency stays >= 1.
+  if (t == 0 && Mp != 0 && (total > UINT64_MAX / Mp || total < N)) bad = 1;
+  __syncthreads();
+  if (bad) {
+    if (t == 0) set_status(status, SKV_ERR_TABLE);
+    if (active)
+      for (uint32_t k = k0; k < k0 + per; ++k) A[k] = k + (uint32_t)(((uint64_t)Mp * k) / N);
+    if (t == 0) A[N] = N + Mp;
+    return;
+  }
+  if (active)
+    for (uint32_t k = k0; k < k0 + per; ++k) {
+      A[k] = k + (uint32_t)(((uint64_t)Mp * H) / total);
+      uint32_t b = bf16 ? unrank_bf16(k) : unrank_e4m3(k);
+      H += hist[b] + 1;
+    }
+  if (t == 0) A[N] = N + Mp;
+}
+
+// ---------------------------------------------------------------- e4m3 bins
+// OCP e4m3 (bias 7, no infinities, NaN = S.1111.111, max 448).  The bin of a
+// code is its round-to-nearest-even preimage with saturation ("原生 FP8 KV
+// 缓存": the FP8 symbols are coded under a bin-integrated Gaussian): edges are
+// midpoints between neighbouring values, 0 splits +-0, +-448 reach +-inf,
+// NaN bins are empty at +-inf.
+__device__ double e4m3_mag(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8u + m), (int)e - 10);
+}
+
+__global__ void k_etab(float2 *__restrict__ etab) {
+  uint32_t b = threadIdx.x;
+  if (b >= 256) return;
+  uint32_t m = b & 0x7Fu;
+  float a, c;
+  if (m == 0x7Fu) {
+    a = c = __builtin_inff();
+  } else {
+    a = m == 0 ? 0.0f : (float)(0.5 * (e4m3_mag(m - 1) + e4m3_mag(m)));
+    c = m == 0x7Eu ? __builtin_inff() : (float)(0.5 * (e4m3_mag(m) + e4m3_mag(m + 1)));
+  }
+  etab[b] = (b & 0x80u) ? make_float2(-c, -a) : make_float2(a, c);
+}
+
+// ---------------------------------------------------------------- scales
+// s_c = RN32(64 / max(sigma_c, 2^-100)): the fp64 quotient of two fp32 values
+// rounds to the same fp32 as the exact quotient (53 >= 2 * 24 + 2).
+// sigma must be finite and >= 0.
+__global__ void k_scale(const float *__restrict__ sigma, float *__restrict__ scale, int64_t n, int32_t *status) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float sg = sigma[i];
+  if (!(sg >= 0.0f) || !__builtin_isfinite(sg)) {
+    set_status(status, SKV_ERR_ARG);
+    sg = 1.0f;
+  }
+  float sp = sg > 0x1p-100f ? sg : 0x1p-100f;
+  scale[i] = (float)(64.0 / (double)sp);
+}
+
+__global__ void k_clear_status(int32_t *status) {
+  if (threadIdx.x == 0) *status = SKV_OK;
+}
+
+hipError_t launch_clear_status(int32_t *status, hipStream_t st) {
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, st, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, const Workspace &ws,
+                        int32_t *status, hipStream_t st) {
+  hipLaunchKernelGGL(k_knots, dim3(1), dim3(1024), 0, st, ws.knots, g.MG);
+  hipLaunchKernelGGL(k_ptable, dim3(1), dim3(1024), 0, st, hist, ws.ptab, g.N, g.Mp,
+                     g.sym_fmt == SKV_SYM_BF16 ? 1 : 0, status);
+  if (g.sym_fmt == SKV_SYM_E4M3) hipLaunchKernelGGL(k_etab, dim3(1), dim3(256), 0, st, ws.etab);
+  int64_t nch = g.rows * g.D;
+  hipLaunchKernelGGL(k_scale, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, sigma, ws.scale, nch, status);
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -1,0 +1,188 @@
+"""Python binding of libskv (include/skv.h): argument marshalling only.
+
+Every step of the coding path runs in the library's HIP kernels; this module
+turns torch tensors into device pointers and the current torch stream into a
+hipStream_t.  There is no fallback: if the library is not built, importing the
+entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libskv.so")
+
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLE = range(7)
+SYM_BF16, SYM_E4M3 = 0, 1
+MU_BF16, MU_F32 = 0, 1
+
+# every function skv.h declares, in declaration order
+EXPORTS = ["skv_status_string", "skv_num_chunks", "skv_encode_bound", "skv_workspace_size",
+           "skv_calib_state_size", "skv_calib_reset", "skv_calib_accumulate", "skv_calib_finalize",
+           "skv_calibrate", "skv_encode", "skv_decode"]
+
+
+class SkvShape(C.Structure):
+    _fields_ = [("layers", C.c_int64), ("kv_heads", C.c_int64), ("tokens", C.c_int64),
+                ("head_dim", C.c_int64), ("sym_fmt", C.c_int32), ("mu_fmt", C.c_int32)]
+
+
+class SkvError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load():
+    """Load libskv.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise SkvError(f"libskv is not built ({LIB_PATH} missing); run __graft_entry__.build()")
+    L = C.CDLL(LIB_PATH)
+    vp, i64, sz, i32p = C.c_void_p, C.c_int64, C.c_size_t, C.c_void_p
+    sp = C.POINTER(SkvShape)
+    L.skv_status_string.restype = C.c_char_p
+    L.skv_status_string.argtypes = [C.c_int]
+    for name in ("skv_num_chunks",):
+        getattr(L, name).argtypes = [sp, C.POINTER(C.c_int64)]
+    for name in ("skv_encode_bound", "skv_workspace_size", "skv_calib_state_size"):
+        getattr(L, name).argtypes = [sp, C.POINTER(C.c_size_t)]
+    L.skv_calib_reset.argtypes = [vp, sp, vp]
+    L.skv_calib_accumulate.argtypes = [vp, sp, vp, vp, vp]
+    L.skv_calib_finalize.argtypes = [vp, sp, vp, vp, vp]
+    L.skv_calibrate.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp]
+    L.skv_encode.argtypes = [sp, vp, vp, vp, vp, vp, sz, vp, vp, sz, i32p, vp]
+    L.skv_decode.argtypes = [sp, vp, sz, vp, vp, vp, vp, vp, vp, sz, i32p, vp]
+    for name in EXPORTS[1:]:
+        getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16) -> SkvShape:
+    return SkvShape(int(layers), int(kv_heads), int(tokens), int(head_dim), int(sym_fmt), int(mu_fmt))
+
+
+def status_string(code: int) -> str:
+    return load().skv_status_string(int(code)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise SkvError(f"{what}: {status_string(rc)} ({rc})")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def num_chunks(sh: SkvShape) -> int:
+    n = C.c_int64(0)
+    _check(load().skv_num_chunks(C.byref(sh), C.byref(n)), "skv_num_chunks")
+    return n.value
+
+
+def _size(fn, sh):
+    n = C.c_size_t(0)
+    _check(getattr(load(), fn)(C.byref(sh), C.byref(n)), fn)
+    return n.value
+
+
+def encode_bound(sh: SkvShape) -> int:
+    return _size("skv_encode_bound", sh)
+
+
+def workspace_size(sh: SkvShape) -> int:
+    return _size("skv_workspace_size", sh)
+
+
+def calib_state_size(sh: SkvShape) -> int:
+    return _size("skv_calib_state_size", sh)
+
+
+# ---- raw entry points: same names and arguments as skv.h ----
+def calib_reset(state, sh: SkvShape, stream=None) -> int:
+    return load().skv_calib_reset(_ptr(state), C.byref(sh), _stream(stream))
+
+
+def calib_accumulate(state, seq_shape: SkvShape, x, mu, stream=None) -> int:
+    return load().skv_calib_accumulate(_ptr(state), C.byref(seq_shape), _ptr(x), _ptr(mu), _stream(stream))
+
+
+def calib_finalize(state, sh: SkvShape, sigma, hist, stream=None) -> int:
+    return load().skv_calib_finalize(_ptr(state), C.byref(sh), _ptr(sigma), _ptr(hist), _stream(stream))
+
+
+def calibrate(seq_shape: SkvShape, n_seq: int, x, mu, sigma, hist, state, stream=None) -> int:
+    return load().skv_calibrate(C.byref(seq_shape), int(n_seq), _ptr(x), _ptr(mu), _ptr(sigma), _ptr(hist),
+                                _ptr(state), _stream(stream))
+
+
+def encode(sh: SkvShape, x, mu, sigma, hist, bits, bits_cap: int, offsets, workspace, workspace_bytes: int,
+           status, stream=None) -> int:
+    return load().skv_encode(C.byref(sh), _ptr(x), _ptr(mu), _ptr(sigma), _ptr(hist), _ptr(bits), int(bits_cap),
+                             _ptr(offsets), _ptr(workspace), int(workspace_bytes), _ptr(status), _stream(stream))
+
+
+def decode(sh: SkvShape, bits, bits_bytes: int, offsets, mu, sigma, hist, x_out, workspace, workspace_bytes: int,
+           status, stream=None) -> int:
+    return load().skv_decode(C.byref(sh), _ptr(bits), int(bits_bytes), _ptr(offsets), _ptr(mu), _ptr(sigma), _ptr(hist), _ptr(x_out),
+                             _ptr(workspace), int(workspace_bytes), _ptr(status), _stream(stream))
+
+
+# ---- buffers sized for a shape (torch allocates, the library fills) ----
+class Buffers:
+    """Device buffers for one cache shape: workspace, stream, offsets, status."""
+
+    def __init__(self, sh: SkvShape, device="cuda"):
+        self.shape = sh
+        self.n_chunks = num_chunks(sh)
+        self.bound = encode_bound(sh)
+        self.ws_bytes = workspace_size(sh)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.bits = torch.empty((self.bound + 15) // 16 * 16, dtype=torch.uint8, device=device)
+        self.offsets = torch.empty(self.n_chunks + 1, dtype=torch.int64, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def encode(self, x, mu, sigma, hist, stream=None) -> None:
+        _check(encode(self.shape, x, mu, sigma, hist, self.bits, self.bits.numel(), self.offsets, self.workspace,
+                      self.ws_bytes, self.status, stream), "skv_encode")
+
+    def decode(self, mu, sigma, hist, x_out, bits=None, offsets=None, stream=None) -> None:
+        bits = self.bits if bits is None else bits
+        offsets = self.offsets if offsets is None else offsets
+        _check(decode(self.shape, bits, bits.numel(), offsets, mu, sigma, hist, x_out, self.workspace,
+                      self.ws_bytes, self.status, stream), "skv_decode")
+
+    def stream_bytes(self) -> int:
+        return int(self.offsets[-1].item())
+
+
+def calibrate_sequences(seq_shape: SkvShape, seqs, device="cuda", stream=None):
+    """sigma and hist from an iterable of (x, mu) device tensors, each of seq_shape."""
+    nch = seq_shape.layers * 2 * seq_shape.kv_heads * seq_shape.head_dim
+    nsym = 65536 if seq_shape.sym_fmt == SYM_BF16 else 256
+    state = torch.empty(calib_state_size(seq_shape), dtype=torch.uint8, device=device)
+    sigma = torch.empty(nch, dtype=torch.float32, device=device)
+    hist = torch.empty(nsym, dtype=torch.int64, device=device)
+    _check(calib_reset(state, seq_shape, stream), "skv_calib_reset")
+    for x, mu in seqs:
+        _check(calib_accumulate(state, seq_shape, x, mu, stream), "skv_calib_accumulate")
+    _check(calib_finalize(state, seq_shape, sigma, hist, stream), "skv_calib_finalize")
+    return sigma, hist
