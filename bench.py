@@ -1,0 +1,255 @@
+"""Benchmark: encode + decode of a Qwen3-32B-shaped bf16 KV cache on one MI355X.
+
+One step = skv_encode + skv_decode of the whole cache (64 layers x {K,V} x 8
+KV heads x 8192 tokens x 128), inputs resident in HBM.  sigma and p_hat are
+calibrated on the GPU first (128 seeded sequences of 512 tokens, not timed).
+Prints one JSON line: raw-KV GB/s of the round trip, per-direction GB/s and
+HBM-roofline fractions, bits/scalar, the roofline of the dominant kernel and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "encode & decode GB/s of raw KV (bf16, e4m3), % HBM roofline; bits/scalar"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="qwen3_32b_bf16")
+    p.add_argument("--calib-seqs", type=int, default=None, help="calibration sequences (default: the workload's 128)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def csrc_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "lossless_kv_cache_scalar_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("csrc_hash") != csrc_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only: the coding path is per-chunk independent and this build "
+              f"measures one GPU's share (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lossless_kv_cache_scalar_amd import build as B
+    from lossless_kv_cache_scalar_amd import skv, synth
+
+    if not B.is_built():
+        B.build()
+    skv.load()
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    nseq = w.calib_seqs if args.calib_seqs is None else args.calib_seqs
+
+    # ---- inputs in HBM (not timed)
+    t0 = time.time()
+    x, mu = synth.generate(w, device=dev)
+    csh = skv.shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+    state = torch.empty(skv.calib_state_size(csh), dtype=torch.uint8, device=dev)
+    sigma = torch.empty(w.n_channels, dtype=torch.float32, device=dev)
+    hist = torch.empty(65536 if w.sym_fmt == 0 else 256, dtype=torch.int64, device=dev)
+    assert skv.calib_reset(state, csh) == skv.OK
+    for j in range(nseq):
+        cx, cm = synth.calibration_set(w, j, device=dev)
+        assert skv.calib_accumulate(state, csh, cx, cm) == skv.OK
+        del cx, cm
+    assert skv.calib_finalize(state, csh, sigma, hist) == skv.OK
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f}s: {w.name}, {w.n_scalars} scalars, {nseq} calibration sequences",
+          file=sys.stderr, flush=True)
+
+    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+    buf = skv.Buffers(sh, device=dev)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        buf.encode(x, mu, sigma, hist, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        buf.decode(mu, sigma, hist, out, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    tstart = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tstart
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms_per_step = wall * 1000.0 / args.steps
+
+    status = int(buf.status.item())
+    exact = bool(torch.equal(out, x))
+    nbytes = buf.stream_bytes()
+    n = w.n_scalars
+    raw = n * w.sym_bytes
+    bits_per_scalar = 8.0 * (nbytes + 8 * (buf.n_chunks + 1)) / n
+    moved = n * (w.sym_bytes + w.mu_bytes) + nbytes  # algorithmic bytes per direction
+    enc_gbps = raw / enc_ms / 1e6
+    dec_gbps = raw / dec_ms / 1e6
+    enc_hbm = moved / enc_ms / 1e6
+    dec_hbm = moved / dec_ms / 1e6
+    dom = "decode" if dec_ms >= enc_ms else "encode"
+    dom_ms = max(dec_ms, enc_ms)
+    kern = "k_decode" if dom == "decode" else "k_encode"
+    traffic = measured_traffic(kern)
+
+    result = {
+        "metric": METRIC,
+        "value": round(raw / ((enc_ms + dec_ms) / 1000.0) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+u64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads, "tokens": w.tokens,
+                   "head_dim": w.head_dim, "symbols": "bf16" if w.sym_fmt == 0 else "e4m3",
+                   "mu": "bf16" if w.mu_fmt == 0 else "f32", "n_scalars": n, "calib_seqs": nseq,
+                   "calib_tokens": w.calib_tokens, "chunk_tokens": 256, "lanes_per_chunk": 64},
+        "encode_GBps": round(enc_gbps, 3),
+        "decode_GBps": round(dec_gbps, 3),
+        "encode_ms": round(enc_ms, 4),
+        "decode_ms": round(dec_ms, 4),
+        "encode_hbm_frac": round(enc_hbm / HBM_PEAK_GBPS, 5),
+        "decode_hbm_frac": round(dec_hbm / HBM_PEAK_GBPS, 5),
+        "bits_per_scalar": round(bits_per_scalar, 5),
+        "compression_ratio": round(16.0 / bits_per_scalar if w.sym_fmt == 0 else 8.0 / bits_per_scalar, 4),
+        "stream_bytes": nbytes,
+        "roundtrip_exact": exact,
+        "status": skv.status_string(status),
+        "roofline": {
+            "kernel": kern,
+            "bound": "hbm",
+            "achieved": round(moved / dom_ms / 1e6, 3),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(moved / dom_ms / 1e6 / HBM_PEAK_GBPS, 5),
+            "traffic": traffic,
+            "bytes_per_launch": moved,
+            "bytes_per_scalar": round(moved / n, 5),
+            "timing": "HIP events around the ABI call on its stream (includes the per-call model build)",
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, mu, sigma, hist, buf, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    if not exact or status != skv.OK:
+        sys.exit(1)
+
+
+def cpu_baseline(w, x, mu, sigma, hist, buf, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of chunks of the same
+    cache; also checks those chunks' GPU bytes against it."""
+    import numpy as np
+
+    from oracle import skvref as R
+
+    cores = max(1, min(os.cpu_count() or 1, 16))
+    rs = R.make_shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+    rsig = sigma.cpu().numpy()
+    rhist = hist.cpu().numpy().view(np.uint64)
+    model = R.Model(w.sym_fmt, rhist)
+    ntb = (w.tokens + 255) // 256
+    rows_per_layer = 2 * w.kv_heads
+
+    def sample(n_rows):
+        # whole (layer, kv, head) rows from the front of the cache, all their chunks
+        xs = x.reshape(-1, w.tokens, w.head_dim)[:n_rows].cpu().numpy()
+        ms = mu.reshape(-1, w.tokens, w.head_dim)[:n_rows].cpu().numpy()
+        xs = np.ascontiguousarray(xs.view(np.uint16 if w.sym_fmt == 0 else np.uint8))
+        ms = np.ascontiguousarray(ms.view(np.uint16) if w.mu_fmt == 0 else ms)
+        shp = R.make_shape(1, n_rows // 2, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt) if n_rows % 2 == 0 else None
+        return xs, ms, shp
+
+    def run(n_rows):
+        xs, ms, shp = sample(n_rows)
+        sig = np.ascontiguousarray(rsig[: n_rows * w.head_dim])
+        t0 = time.perf_counter()
+        bits, offs = model.encode(shp, xs, ms, sig, nthreads=cores)
+        t1 = time.perf_counter()
+        dec, st = model.decode(shp, bits, offs, ms, sig, nthreads=cores)
+        t2 = time.perf_counter()
+        return xs, bits, offs, dec, st, t1 - t0, t2 - t1
+
+    # size the sample: one row first, then as many rows as fit the time budget
+    _, _, _, _, _, te, td = run(2)
+    per_row = (te + td) / 2
+    n_rows = int(max(2, min(w.layers * rows_per_layer, seconds / max(per_row, 1e-6))))
+    n_rows -= n_rows % 2
+    xs, bits, offs, dec, st, te, td = run(n_rows)
+    n = xs.size
+    raw = n * w.sym_bytes
+    # the sample's chunks are the GPU stream's first chunks: compare bytes
+    nchunks = n_rows * ntb
+    goffs = buf.offsets[: nchunks + 1].cpu().numpy().view(np.uint64)
+    gbits = buf.bits[: int(goffs[-1])].cpu().numpy()
+    same = bool(np.array_equal(goffs, offs) and np.array_equal(gbits, bits))
+    return {
+        "value": round(raw / (te + td) / 1e9, 5),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{n_rows} of {w.layers * rows_per_layer} (layer, kv, head) rows = {nchunks} chunks, "
+                  f"{n} scalars, encode + decode",
+        "encode_GBps": round(raw / te / 1e9, 5),
+        "decode_GBps": round(raw / td / 1e9, 5),
+        "seconds": round(te + td, 3),
+        "gpu_bytes_match_oracle": same,
+        "oracle_roundtrip_exact": bool(st == R.OK and np.array_equal(dec, xs)),
+    }
+
+
+if __name__ == "__main__":
+    main()
