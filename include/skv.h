@@ -153,7 +153,8 @@ int skv_encode(const skv_shape *shape, const void *x, const void *mu, const floa
  * Decode a cache encoded by skv_encode with the same shape, mu, sigma and hist
  * (the model is not stored in the stream: both ends rebuild it, "什么能预测 KV
  * 缓存").
- *   bits     (device) the stream, bits_bytes readable bytes; no read leaves
+ *   bits     (device) the stream, 4-byte aligned, bits_bytes readable bytes
+ *            (a multiple of 4; skv_encode's buffer qualifies); no read leaves
  *            [bits, bits + bits_bytes) whatever offsets and headers say
  *   offsets  (device) u64 [n_chunks + 1] (a chunk outside bits_bytes, or with
  *            offsets[c+1] < offsets[c], decodes as corrupt)

@@ -54,7 +54,7 @@ int make_geo(const skv_shape *sh, Geo &g) {
 }
 
 struct Layout {
-  size_t knots, ptab, etab, scale, lens, sizes, scratch, total;
+  size_t knots, ptab, a16, abase, aflag, uinv, etab, scale, lens, sizes, scratch, total;
 };
 
 Layout layout(const Geo &g) {
@@ -62,6 +62,10 @@ Layout layout(const Geo &g) {
   size_t o = 0;
   L.knots = o; o = align_up(o + sizeof(float2) * kNKnot);
   L.ptab = o;  o = align_up(o + sizeof(uint32_t) * (g.N + 1));
+  L.a16 = o;   o = align_up(o + sizeof(uint16_t) * kNWin * kWinEntries);
+  L.abase = o; o = align_up(o + sizeof(uint32_t) * (kNWin + 1));
+  L.aflag = o; o = align_up(o + sizeof(int32_t));
+  L.uinv = o;  o = align_up(o + sizeof(float2) * (kNInv + 1));
   L.etab = o;  o = align_up(o + sizeof(float2) * 256);
   L.scale = o; o = align_up(o + sizeof(float) * (size_t)(g.rows * g.D));
   L.lens = o;  o = align_up(o + sizeof(uint32_t) * (size_t)g.n_chunks * kLanes);
@@ -77,6 +81,10 @@ Workspace carve(const Geo &g, void *base) {
   Workspace w;
   w.knots = reinterpret_cast<float2 *>(b + L.knots);
   w.ptab = reinterpret_cast<uint32_t *>(b + L.ptab);
+  w.a16 = reinterpret_cast<uint16_t *>(b + L.a16);
+  w.abase = reinterpret_cast<uint32_t *>(b + L.abase);
+  w.aflag = reinterpret_cast<int32_t *>(b + L.aflag);
+  w.uinv = reinterpret_cast<float2 *>(b + L.uinv);
   w.etab = reinterpret_cast<float2 *>(b + L.etab);
   w.scale = reinterpret_cast<float *>(b + L.scale);
   w.lens = reinterpret_cast<uint32_t *>(b + L.lens);
@@ -197,6 +205,7 @@ extern "C" int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bi
   if (e != SKV_OK) return e;
   if (!bits || !offsets || !mu || !sigma || !hist || !x_out || !workspace || !status) return SKV_ERR_ARG;
   if (!aligned16(mu) || !aligned16(x_out) || !aligned16(workspace)) return SKV_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(bits) & 3u) || (bits_bytes & 3u)) return SKV_ERR_ARG;
   if (workspace_bytes < layout(g).total) return SKV_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Workspace ws = carve(g, workspace);

@@ -1,12 +1,29 @@
 // skv_decode.hip -- decode a range-coded KV cache on gfx950.
 //
-// One wavefront per chunk, lane l decodes substream l: the same 8-scalar
-// groups the encoder gave it, so the decoded symbols of a wave step are one
-// contiguous 1 KB (bf16) store.  The model is rebuilt from (mu, sigma, hist),
-// as both ends of the coder do ("Speculative KV coding", "什么能预测 KV 缓存").
-#include "skv_internal.hpp"
+// Persistent grid, one 1024-thread block per CU with the model's tables in
+// LDS (knots, the inverse of the Gaussian pair's CDF, and the bf16 p_hat table
+// for ranks 8192..57343, i.e. every value below 2^64 in magnitude; rarer ranks
+// read the global copy).  Each wavefront decodes whole chunks; lane l decodes
+// substream l, i.e. the same 8-scalar groups the encoder gave it, so one wave
+// step stores 1 KB of decoded bf16 contiguously.  The model is rebuilt from
+// (mu, sigma, hist), as both ends of the coder do ("Speculative KV coding",
+// "什么能预测 KV 缓存").
+//
+// Symbol search.  The decoder needs the unique symbol s with
+// r * cum_lo(s) <= d < r * cum_hi(s).  A guess comes from inverting the
+// Gaussian pair's CDF at t ~ d / r (fp32, approximate on purpose); the guess
+// is then verified with the exact integer model and the exact 48-bit
+// products, and a miss is corrected by a galloping search over ranks.  Any
+// exact search returns the same symbol, so the output does not depend on the
+// guess.
+#include "skv_modeldev.hpp"
 
 namespace skv {
+
+constexpr int kDecBlock = 1024;
+constexpr int kDecWaves = kDecBlock / 64;
+constexpr uint32_t kDecW0 = 128;  // first LDS window: rank 8192
+constexpr uint32_t kDecNW = 768;  // windows in LDS: ranks 8192 .. 57343
 
 struct DecArgs {
   Geo g;
@@ -16,164 +33,340 @@ struct DecArgs {
   const void *mu;
   const float2 *knots;
   const uint32_t *ptab;
+  const uint16_t *a16;
+  const uint32_t *abase;
+  const int32_t *aflag;
+  const float2 *uinv;
   const float2 *etab;
   const float *scale;
+  float inv_step;  // kNInv / MG
   void *x_out;
   int32_t *status;
 };
 
-// cum(k) = A(k) + Cg(u(lower edge of unrank(k))), cum(N) = T
-template <int SYM>
-__device__ __forceinline__ uint32_t cum_rank(const DecArgs &a, const float2 *kn, const float2 *etab_s,
-                                             const uint32_t *ptab_s, uint32_t k, float mu, float s) {
-  if (SYM == SKV_SYM_BF16) {
-    if (k >= 65536u) return 1u << 24;
-    return a.ptab[k] + cg_eval(kn, u_of(bf16_lo_edge(unrank_bf16(k)), mu, s));
+// Bits of one substream, most significant first; bytes past its end read as 0.
+struct BitReader {
+  const uint8_t *bits;
+  uint64_t ib;   // next bits, left-aligned
+  int nib;       // valid bits in ib
+  uint64_t wp;   // next aligned word to load
+  uint64_t end;  // substream end (exclusive)
+
+  __device__ __forceinline__ void refill() {  // needs nib <= 32
+    uint32_t w = 0;
+    if (wp < end) {
+      w = __builtin_bswap32(*reinterpret_cast<const uint32_t *>(bits + wp));
+      const uint64_t valid = end - wp;
+      if (valid < 4) w &= ~(0xFFFFFFFFu >> (8 * (uint32_t)valid));
+    }
+    ib |= (uint64_t)w << (32 - nib);
+    nib += 32;
+    wp += 4;
+  }
+  __device__ __forceinline__ void init(const uint8_t *b, uint64_t st, uint64_t e) {
+    bits = b;
+    end = e;
+    wp = st & ~3ull;
+    ib = 0;
+    nib = 0;
+    refill();
+    const int skip = 8 * (int)(st & 3);
+    ib <<= skip;
+    nib -= skip;
+  }
+  // n in {0, 8, 16, 24}, after ensure(n)
+  __device__ __forceinline__ uint32_t take(uint32_t n) {
+    const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)(ib >> 32), (0u - n) & 31u, n);
+    ib <<= n;
+    nib -= (int)n;
+    return v;
+  }
+  __device__ __forceinline__ void ensure(uint32_t n) {
+    if (nib < (int)n) refill();
+  }
+};
+
+// bf16 pattern of x, rounded to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// e4m3 pattern near e (round to nearest, saturating): a first guess only
+__device__ __forceinline__ uint32_t e4m3_guess(float e) {
+  const uint32_t sgn = (__float_as_uint(e) >> 24) & 0x80u;
+  const float a = __builtin_fminf(__builtin_fabsf(e), 448.0f);
+  uint32_t code;
+  if (a >= 0x1p-6f) code = ((__float_as_uint(a) + 0x7FFFFu) >> 20) - (120u << 3);
+  else code = (uint32_t)__builtin_rintf(a * 512.0f);
+  return sgn | min(code, 0x7Eu);
+}
+
+// A(k) for a guess: the LDS window clamps k (an approximate value is enough)
+template <int SYM, int TAB>
+__device__ __forceinline__ uint32_t a_guess(const ModelTabs &t, uint32_t k) {
+  if (SYM != SKV_SYM_BF16) return t.ab[k];
+  if (TAB == kTabGlobal) return t.ptab[k];
+  const uint32_t kc = min(max(k, 64u * kDecW0), 64u * (kDecW0 + kDecNW) - 1u);
+  const uint32_t wl = (kc >> 6) - kDecW0;
+  return t.ab[wl] + t.a16[65u * wl + (kc & 63u)];
+}
+
+// The symbol whose bin holds the value where the Gaussian pair's CDF reaches
+// t - A(k): the inverse table gives the knot coordinate, mu + u sigma / 64 the
+// value, and rounding to the symbol format the guess.
+template <int SYM, int TAB>
+__device__ __forceinline__ uint32_t guess_symbol(const ModelTabs &t, const float2 *uinv, float tq, uint32_t k,
+                                                 float inv_step, float sinv, float m) {
+  float mf = (tq - (float)a_guess<SYM, TAB>(t, k)) * inv_step;
+  mf = __builtin_fminf(__builtin_fmaxf(mf, 0.0f), (float)kNInv - 0.5f);
+  const int ii = (int)mf;
+  const float2 ud = uinv[ii];
+  const float uu = __builtin_fmaf(mf - (float)ii, ud.y, ud.x);
+  const float e = __builtin_fmaf(uu, sinv, m);
+  return SYM == SKV_SYM_BF16 ? bf16_rne_bits(e) : e4m3_guess(e);
+}
+
+template <int SYM, int MU>
+struct MuGroup {
+  uint4 v0, v1;
+  __device__ __forceinline__ void load(const void *mu, int64_t i0) {
+    if (MU == SKV_MU_BF16) {
+      v0 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(mu) + i0);
+    } else {
+      const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(mu) + i0);
+      v0 = p[0];
+      v1 = p[1];
+    }
+  }
+  __device__ __forceinline__ float get(int j) const {
+    if (MU == SKV_MU_BF16) {
+      const uint32_t w[4] = {v0.x, v0.y, v0.z, v0.w};
+      return mu_from_bf16((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+    }
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    return mu_from_f32(__uint_as_float(w[j]));
+  }
+};
+
+// The exact rank: largest k with r * (cum(k) << up) <= d, bracketed from the
+// guess kg (below: the answer is under kg; otherwise it is above kg).
+template <int SYM, int TAB>
+__device__ uint32_t search_rank(const ModelTabs &t, uint32_t kg, bool below, uint64_t d, uint32_t r, int up,
+                                float m, float s) {
+  const uint32_t N = SYM == SKV_SYM_BF16 ? 65536u : 256u;
+  auto leq = [&](uint32_t k) -> bool { return mul24(r, cum_rank<SYM, TAB>(t, k, m, s) << up) <= d; };
+  uint32_t lo, hi;
+  if (below) {
+    hi = kg;
+    uint32_t step = 1;
+    for (;;) {
+      const uint32_t p = hi > step ? hi - step : 0u;
+      if (p == 0 || leq(p)) {
+        lo = p;
+        break;
+      }
+      hi = p;
+      step <<= 1;
+    }
   } else {
-    if (k >= 256u) return 1u << 16;
-    return ptab_s[k] + cg_eval(kn, u_of(etab_s[unrank_e4m3(k)].x, mu, s));
+    lo = kg + 1;
+    hi = N;
+    if (lo >= N) return N - 1;  // beyond the last symbol: a corrupt stream
+    uint32_t step = 1;
+    for (;;) {
+      const uint32_t p = lo + step;
+      if (p >= N) break;
+      if (leq(p)) {
+        lo = p;
+        step <<= 1;
+      } else {
+        hi = p;
+        break;
+      }
+    }
+  }
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (leq(mid)) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <int SYM, int MU, int TAB>
+__device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs &t, const float2 *uinv) {
+  constexpr bool BF = SYM == SKV_SYM_BF16;
+  constexpr int up = BF ? 0 : 8;
+  const Geo &g = a.g;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int64_t chunk = (int64_t)blockIdx.x * kDecWaves + wave; chunk < g.n_chunks;
+       chunk += (int64_t)gridDim.x * kDecWaves) {
+    const int64_t row = chunk / g.ntb, blk = chunk - row * g.ntb;
+    const int64_t tok = min<int64_t>(kChunkTokens, g.tokens - blk * kChunkTokens);
+    const int ngroups = (int)(tok * g.D / kGroup);
+    const int64_t base = (row * g.tokens + blk * kChunkTokens) * g.D;
+
+    // ---- header: lane lengths, their prefix, consistency with the offsets
+    const uint64_t o0 = a.offsets[chunk], o1 = a.offsets[chunk + 1];
+    const uint64_t nbytes = o1 >= o0 ? o1 - o0 : 0;
+    bool corrupt = o1 < o0 || o1 > a.bits_bytes || nbytes < (uint64_t)kHeaderBytes;
+    uint32_t len = 0;
+    if (!corrupt) len = (uint32_t)a.bits[o0 + 2 * lane] | ((uint32_t)a.bits[o0 + 2 * lane + 1] << 8);
+    uint32_t pre = len;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(pre, off, 64);
+      if (lane >= off) pre += v;
+    }
+    const uint32_t total = __shfl(pre, 63, 64);
+    uint64_t start = (uint64_t)kHeaderBytes + (pre - len);
+    if (!corrupt && (uint64_t)kHeaderBytes + total != nbytes) corrupt = true;
+    if (len == 0) corrupt = true;
+    if (corrupt) len = 0;  // a chunk outside the buffer reads nothing
+    if (start > nbytes) start = nbytes;
+    if (start + len > nbytes) len = (uint32_t)(nbytes - start);
+
+    const int d0 = (kGroup * lane) % (int)g.D;
+    float s[kGroup], sinv[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      s[j] = a.scale[row * g.D + d0 + j];
+      sinv[j] = __builtin_amdgcn_rcpf(s[j]);  // ~sigma / 64, guesses only
+    }
+
+    // a corrupt chunk reads nothing: its reader starts and ends at byte 0
+    const uint64_t st = corrupt ? 0 : o0 + start;
+    BitReader br;
+    br.init(a.bits, st, st + len);
+    br.ensure(24);
+    uint64_t d = (uint64_t)br.take(24) << 24;
+    br.ensure(24);
+    d |= br.take(24);
+    uint64_t range = kW48;
+    uint32_t shifted = 0;  // renormalisation bytes consumed
+
+    MuGroup<SYM, MU> cur;
+    if (lane < ngroups) cur.load(a.mu, base + (int64_t)lane * kGroup);
+    for (int grp = lane; grp < ngroups; grp += kLanes) {
+      const int64_t i0 = base + (int64_t)grp * kGroup;
+      MuGroup<SYM, MU> nxt;
+      if (grp + kLanes < ngroups) nxt.load(a.mu, i0 + kLanes * kGroup);
+      uint32_t out[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const float m = cur.get(j), sj = s[j];
+        const uint32_t r = (uint32_t)(range >> 24);
+        // ---- guess: invert the Gaussian pair's CDF at t - A(k), first with k the
+        // rank of mu, then with k the rank of that first guess (the one-count
+        // floor makes A(k) grow by one per rank, which matters near zero)
+        const float tq = (float)(uint32_t)(d >> 16) * (65536.0f * __builtin_amdgcn_rcpf((float)(r << up)));
+        uint32_t kmu;
+        if (BF) kmu = rank_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : (__float_as_uint(m) >> 16));
+        else kmu = rank_e4m3(e4m3_guess(m));
+        uint32_t gs = guess_symbol<SYM, TAB>(t, uinv, tq, kmu, a.inv_step, sinv[j], m);
+        gs = guess_symbol<SYM, TAB>(t, uinv, tq, BF ? rank_bf16(gs) : rank_e4m3(gs), a.inv_step, sinv[j], m);
+        // ---- verify exactly
+        uint32_t clo, chi;
+        model_pair<SYM, TAB>(t, gs, m, sj, clo, chi);
+        uint64_t plo = mul24(r, clo << up), pf = mul24(r, (chi - clo) << up);
+        unsigned int b0, b1;
+        uint32_t dl = __builtin_subc((uint32_t)d, (uint32_t)plo, 0u, &b0);
+        uint32_t dh = __builtin_subc((uint32_t)(d >> 32), (uint32_t)(plo >> 32), b0, &b1);
+        uint64_t dd = ((uint64_t)dh << 32) | dl;
+        bool ok = b1 == 0 && dd < pf;
+        if (__builtin_expect(__any(!ok), 0)) {
+          if (!ok) {
+            const uint32_t kg = BF ? rank_bf16(gs) : rank_e4m3(gs);
+            const uint32_t ks = search_rank<SYM, TAB>(t, kg, b1 != 0, d, r, up, m, sj);
+            gs = BF ? unrank_bf16(ks) : unrank_e4m3(ks);
+            model_pair<SYM, TAB>(t, gs, m, sj, clo, chi);
+            plo = mul24(r, clo << up);
+            pf = mul24(r, (chi - clo) << up);
+            dd = d - plo;
+            if (d < plo || dd >= pf) {  // no symbol holds d: corrupt stream
+              corrupt = true;
+              dd = 0;
+            }
+          }
+        }
+        // ---- update and renormalise
+        const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & ~7u;
+        br.ensure(n8);
+        d = (dd << n8) | br.take(n8);
+        range = pf << n8;
+        shifted += n8 >> 3;
+        out[j] = gs;
+      }
+      if (BF) {
+        uint4 v;
+        v.x = out[0] | (out[1] << 16);
+        v.y = out[2] | (out[3] << 16);
+        v.z = out[4] | (out[5] << 16);
+        v.w = out[6] | (out[7] << 16);
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.x_out) + i0) = v;
+      } else {
+        uint2 v;
+        v.x = out[0] | (out[1] << 8) | (out[2] << 16) | (out[3] << 24);
+        v.y = out[4] | (out[5] << 8) | (out[6] << 16) | (out[7] << 24);
+        *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(a.x_out) + i0) = v;
+      }
+      cur = nxt;
+    }
+    // a substream of n renormalisations holds n + 1 bytes
+    if (shifted + 1 != len) corrupt = true;
+    if (corrupt) set_status(a.status, SKV_ERR_CORRUPT);
   }
 }
 
 template <int SYM, int MU>
-__global__ __launch_bounds__(256) void k_decode(DecArgs a) {
+__global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
+  constexpr bool BF = SYM == SKV_SYM_BF16;
   __shared__ float2 s_kn[kNKnot];
-  __shared__ float2 s_etab[SYM == SKV_SYM_E4M3 ? 256 : 1];
-  __shared__ uint32_t s_ptab[SYM == SKV_SYM_E4M3 ? 257 : 1];
-  for (int i = threadIdx.x; i < kNKnot; i += blockDim.x) s_kn[i] = a.knots[i];
-  if (SYM == SKV_SYM_E4M3) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) s_etab[i] = a.etab[i];
-    for (int i = threadIdx.x; i < 257; i += blockDim.x) s_ptab[i] = a.ptab[i];
+  __shared__ float2 s_ui[kNInv + 1];
+  __shared__ uint32_t s_a16w[BF ? kDecNW * kWinEntries / 2 : 1];
+  __shared__ uint32_t s_ab[BF ? kDecNW + 1 : 257];
+  __shared__ float2 s_et[BF ? 1 : 256];
+
+  const bool win = BF ? *a.aflag != 0 : true;
+  for (int i = threadIdx.x; i < kNKnot; i += kDecBlock) s_kn[i] = a.knots[i];
+  for (int i = threadIdx.x; i <= kNInv; i += kDecBlock) s_ui[i] = a.uinv[i];
+  if (BF) {
+    if (win) {
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.a16 + kDecW0 * kWinEntries);
+      for (int i = threadIdx.x; i < (int)(kDecNW * kWinEntries / 2); i += kDecBlock) s_a16w[i] = src[i];
+      for (int i = threadIdx.x; i <= (int)kDecNW; i += kDecBlock) s_ab[i] = a.abase[kDecW0 + i];
+    }
+  } else {
+    for (int i = threadIdx.x; i < 257; i += kDecBlock) s_ab[i] = a.ptab[i];
+    for (int i = threadIdx.x; i < 256; i += kDecBlock) s_et[i] = a.etab[i];
   }
   __syncthreads();
+  const ModelTabs t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, a.ptab, s_et, kDecW0, kDecNW};
+  if (!BF) decode_chunks<SYM, MU, kTabLdsAll>(a, t, s_ui);
+  else if (win) decode_chunks<SYM, MU, kTabLdsWin>(a, t, s_ui);
+  else decode_chunks<SYM, MU, kTabGlobal>(a, t, s_ui);
+}
 
-  const Geo &g = a.g;
-  const int lane = threadIdx.x & 63;
-  const int64_t chunk = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (chunk >= g.n_chunks) return;
-  const int64_t row = chunk / g.ntb, blk = chunk % g.ntb;
-  const int64_t tok = min<int64_t>(kChunkTokens, g.tokens - blk * kChunkTokens);
-  const int64_t ngroups = tok * g.D / kGroup;
-  const int64_t base = (row * g.tokens + blk * kChunkTokens) * g.D;
-  const uint32_t N = SYM == SKV_SYM_BF16 ? 65536u : 256u;
-  const uint32_t T = SYM == SKV_SYM_BF16 ? (1u << 24) : (1u << 16);
-  const int up = SYM == SKV_SYM_BF16 ? 0 : 8;
-
-  // ---- header: lane lengths, their prefix, and consistency with the offsets
-  const uint64_t o0 = a.offsets[chunk], o1 = a.offsets[chunk + 1];
-  const uint64_t nbytes = o1 >= o0 ? o1 - o0 : 0;
-  bool corrupt = o1 < o0 || o1 > a.bits_bytes || nbytes < (uint64_t)kHeaderBytes;
-  uint32_t len = 0;
-  if (!corrupt) len = (uint32_t)a.bits[o0 + 2 * lane] | ((uint32_t)a.bits[o0 + 2 * lane + 1] << 8);
-  uint32_t pre = len;  // inclusive prefix over lanes
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t v = __shfl_up(pre, off, 64);
-    if (lane >= off) pre += v;
+static int dec_cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
   }
-  const uint32_t total = __shfl(pre, 63, 64);
-  uint64_t start = (uint64_t)kHeaderBytes + (pre - len);
-  if (!corrupt && (uint64_t)kHeaderBytes + total != nbytes) corrupt = true;
-  if (len == 0) corrupt = true;
-  // keep every substream inside the chunk whatever the header says
-  if (corrupt) len = 0;  // a chunk outside the buffer reads nothing
-  if (start > nbytes) start = nbytes;
-  if (start + len > nbytes) len = (uint32_t)(nbytes - start);
-  const uint8_t *src = a.bits + o0 + start;
-
-  const int d0 = (int)((kGroup * lane) % g.D);
-  float s[kGroup];
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) s[j] = a.scale[row * g.D + d0 + j];
-
-  uint32_t pos = 0;
-  auto next_byte = [&]() -> uint64_t {
-    uint64_t v = pos < len ? src[pos] : 0;
-    ++pos;
-    return v;
-  };
-  uint64_t d = 0, range = kW48;
-  for (int i = 0; i < 6; ++i) d = (d << 8) | next_byte();
-  uint32_t shifts = 0;
-
-  for (int64_t grp = lane; grp < ngroups; grp += kLanes) {
-    const int64_t i0 = base + grp * kGroup;
-    float mu[kGroup];
-    if (MU == SKV_MU_BF16) {
-      uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.mu) + i0);
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mu[2 * j] = mu_from_bf16(w[j] & 0xFFFFu);
-        mu[2 * j + 1] = mu_from_bf16(w[j] >> 16);
-      }
-    } else {
-      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.mu) + i0);
-      float4 v0 = p[0], v1 = p[1];
-      float m8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mu[j] = mu_from_f32(m8[j]);
-    }
-    uint32_t out[kGroup];
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const uint64_t r = range >> 24;
-      const uint64_t q = r << up;
-      // t = floor(d / q): the fp64 quotient of exact integers is within one of it
-      uint64_t t = q ? (uint64_t)((double)d / (double)q) : 0;
-      if (q) {
-        uint64_t tq = t * q;
-        if (tq > d) t -= 1;
-        else if (tq + q <= d) t += 1;
-      }
-      if (t >= T) {
-        corrupt = true;
-        t = T - 1;
-      }
-      // the unique rank k with cum(k) <= t < cum(k + 1), by bisection
-      uint32_t lo = 0, hi = N;
-      while (hi - lo > 1) {
-        uint32_t mid = (lo + hi) >> 1;
-        if (cum_rank<SYM>(a, s_kn, s_etab, s_ptab, mid, mu[j], s[j]) <= t) lo = mid; else hi = mid;
-      }
-      const uint32_t c = cum_rank<SYM>(a, s_kn, s_etab, s_ptab, lo, mu[j], s[j]);
-      const uint32_t f = cum_rank<SYM>(a, s_kn, s_etab, s_ptab, lo + 1, mu[j], s[j]) - c;
-      d -= r * ((uint64_t)c << up);
-      range = r * ((uint64_t)f << up);
-      for (int it = 0; it < 6 && range < kTop40; ++it) {
-        d = ((d << 8) | next_byte()) & kW48;
-        range <<= 8;
-        ++shifts;
-      }
-      out[j] = SYM == SKV_SYM_BF16 ? unrank_bf16(lo) : unrank_e4m3(lo);
-    }
-    if (SYM == SKV_SYM_BF16) {
-      uint4 v;
-      v.x = out[0] | (out[1] << 16);
-      v.y = out[2] | (out[3] << 16);
-      v.z = out[4] | (out[5] << 16);
-      v.w = out[6] | (out[7] << 16);
-      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.x_out) + i0) = v;
-    } else {
-      uint2 v;
-      v.x = out[0] | (out[1] << 8) | (out[2] << 16) | (out[3] << 24);
-      v.y = out[4] | (out[5] << 8) | (out[6] << 16) | (out[7] << 24);
-      *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(a.x_out) + i0) = v;
-    }
-  }
-  // a substream of n renormalisations holds n + 1 bytes
-  if (shifts + 1 != len) corrupt = true;
-  if (corrupt) set_status(a.status, SKV_ERR_CORRUPT);
+  return n;
 }
 
 template <int SYM, int MU>
 static void launch_dec_kernel(const DecArgs &a, hipStream_t st) {
-  unsigned blocks = (unsigned)((a.g.n_chunks + kWavesPerBlock - 1) / kWavesPerBlock);
-  hipLaunchKernelGGL((k_decode<SYM, MU>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, st, a);
+  const int64_t need = (a.g.n_chunks + kDecWaves - 1) / kDecWaves;
+  const int64_t cus = dec_cu_count();
+  const unsigned blocks = (unsigned)(need < cus ? need : cus);
+  hipLaunchKernelGGL((k_decode<SYM, MU>), dim3(blocks), dim3(kDecBlock), 0, st, a);
 }
 
 hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes, const uint64_t *offsets,
                          const void *mu, const Workspace &ws, void *x_out, int32_t *status, hipStream_t st) {
-  DecArgs a{g, bits, bits_bytes, offsets, mu, ws.knots, ws.ptab, ws.etab, ws.scale, x_out, status};
+  DecArgs a{g, bits, bits_bytes, offsets, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.uinv, ws.etab,
+            ws.scale, (float)kNInv / (float)g.MG, x_out, status};
   if (g.sym_fmt == SKV_SYM_BF16) {
     if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_BF16, SKV_MU_BF16>(a, st);
     else launch_dec_kernel<SKV_SYM_BF16, SKV_MU_F32>(a, st);

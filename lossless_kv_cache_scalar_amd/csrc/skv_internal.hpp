@@ -24,6 +24,14 @@ constexpr int kUMax = 1024;       // knots cover |z| <= 16
 constexpr int kNKnot = 2 * kUMax + 1;
 constexpr int kHeaderBytes = 2 * kLanes;
 constexpr int kWavesPerBlock = 4;
+// bf16 p_hat table as held in LDS: windows of 64 ranks, each stored as 65 u16
+// offsets from the window's u32 base (the 65th is the next window's first rank),
+// so A(k) and A(k+1) come from one window: 133 KB + 4 KB for all 65536 ranks.
+constexpr int kWinRanks = 64;
+constexpr int kWinEntries = kWinRanks + 1;
+constexpr int kNWin = 65536 / kWinRanks;
+// inverse of the Gaussian-pair CDF (counts -> knot coordinate), decoder guesses
+constexpr int kNInv = 2048;
 constexpr uint64_t kW48 = 0xFFFFFFFFFFFFull;
 constexpr uint64_t kTop40 = 1ull << 40;
 
@@ -44,6 +52,10 @@ struct Geo {
 struct Workspace {
   float2 *knots;      // kNKnot (K_j, K_{j+1} - K_j)
   uint32_t *ptab;     // N + 1: A(k) = k + Qhat(k)
+  uint16_t *a16;      // kNWin * kWinEntries: A(64w + j) - A(64w) (bf16)
+  uint32_t *abase;    // kNWin + 1: A(64w)
+  int32_t *aflag;     // 1 when every window's offsets fit 16 bits
+  float2 *uinv;       // kNInv + 1: (u, du) at y = m * MG / kNInv
   float2 *etab;       // 256 e4m3 bins (lo, hi), indexed by pattern
   float *scale;       // per channel: RN32(64 / max(sigma, 2^-100))
   uint32_t *lens;     // n_chunks * 64 substream lengths (encode)

@@ -43,27 +43,46 @@ __global__ __launch_bounds__(1024) void k_knots(float2 *__restrict__ out, uint32
 // p_hat: the calibration symbol histogram, +1 smoothed, in rank order
 // ("早期结果": the empirical bf16 symbol distribution).  H(0) = 0,
 // H(k+1) = H(k) + hist[unrank(k)] + 1, Qhat(k) = floor(Mp H(k) / H(N));
-// A(k) = k + Qhat(k) carries the one-count floor of every symbol.
-// One block of 1024 threads, each owning N / 1024 consecutive ranks (N = 256
-// uses the first 256 threads, one rank each).
+// A(k) = k + Qhat(k) carries the one-count floor of every symbol.  The
+// quotient is exact: an fp64 estimate, then integer correction steps.
+// Domain: Mp * H(N) < 2^62, else SKV_ERR_TABLE.
+__device__ __forceinline__ uint64_t floor_div(uint64_t num, uint64_t den) {
+  uint64_t q = (uint64_t)((double)num / (double)den);  // within 2 of the quotient
+#pragma unroll
+  for (int it = 0; it < 3; ++it)
+    if (q > 0 && q * den > num) --q;
+#pragma unroll
+  for (int it = 0; it < 3; ++it)
+    if ((q + 1) * den <= num) ++q;
+  return q;
+}
+
+// One block of 1024 threads; thread t owns window t: ranks 64t .. 64t + 63
+// (bf16: all 1024 windows; e4m3: the first 4).  Writes the full table A and,
+// for bf16, the LDS image: base A(64t) and 65 u16 offsets A(64t + j) - A(64t),
+// j = 0..64, flagging a window whose offsets do not fit 16 bits.
 __global__ __launch_bounds__(1024) void k_ptable(const uint64_t *__restrict__ hist, uint32_t *__restrict__ A,
-                                                 uint32_t N, uint32_t Mp, int bf16, int32_t *status) {
+                                                 uint16_t *__restrict__ a16, uint32_t *__restrict__ abase,
+                                                 int32_t *__restrict__ aflag, uint32_t N, uint32_t Mp, int bf16,
+                                                 int32_t *status) {
   __shared__ uint64_t part[1024];
-  __shared__ int bad;
+  __shared__ int bad, narrow;
   const int t = threadIdx.x;
-  const uint32_t per = N >= 1024 ? N / 1024 : 1;
-  const uint32_t k0 = t * per;
-  const bool active = k0 < N;
+  const uint32_t nwin = N / kWinRanks;
+  const bool active = (uint32_t)t < nwin;
+  const uint32_t k0 = (uint32_t)t * kWinRanks;
   uint64_t s = 0;
   if (active)
-    for (uint32_t k = k0; k < k0 + per; ++k) {
-      uint32_t b = bf16 ? unrank_bf16(k) : unrank_e4m3(k);
-      s += hist[b] + 1;
+    for (int j = 0; j < kWinRanks; ++j) {
+      uint32_t k = k0 + j;
+      s += hist[bf16 ? unrank_bf16(k) : unrank_e4m3(k)] + 1;
     }
   part[t] = s;
-  if (t == 0) bad = 0;
+  if (t == 0) {
+    bad = 0;
+    narrow = 0;
+  }
   __syncthreads();
-  // inclusive scan (Hillis-Steele) over the 1024 partial sums
   for (int off = 1; off < 1024; off <<= 1) {
     uint64_t v = t >= off ? part[t - off] : 0;
     __syncthreads();
@@ -72,24 +91,59 @@ __global__ __launch_bounds__(1024) void k_ptable(const uint64_t *__restrict__ hi
   }
   const uint64_t total = part[1023];
   uint64_t H = part[t] - s;  // exclusive prefix
-  // Mp * H(N) must fit 64 bits; a histogram that large (or one whose counts
-  // wrapped) falls back to the uniform table so every frequency stays >= 1.
-  if (t == 0 && Mp != 0 && (total > UINT64_MAX / Mp || total < N)) bad = 1;
+  if (t == 0 && (total < N || (Mp != 0 && total > (1ull << 62) / Mp))) bad = 1;
   __syncthreads();
-  if (bad) {
+  if (bad) {  // uniform table so that every frequency stays >= 1
     if (t == 0) set_status(status, SKV_ERR_TABLE);
-    if (active)
-      for (uint32_t k = k0; k < k0 + per; ++k) A[k] = k + (uint32_t)(((uint64_t)Mp * k) / N);
-    if (t == 0) A[N] = N + Mp;
+    for (uint32_t k = t; k <= N; k += blockDim.x) A[k] = k + (uint32_t)(((uint64_t)Mp * k) / N);
+    if (t == 0) *aflag = 0;
     return;
   }
-  if (active)
-    for (uint32_t k = k0; k < k0 + per; ++k) {
-      A[k] = k + (uint32_t)(((uint64_t)Mp * H) / total);
-      uint32_t b = bf16 ? unrank_bf16(k) : unrank_e4m3(k);
-      H += hist[b] + 1;
+  if (active) {
+    uint32_t a0 = 0;
+    for (int j = 0; j <= kWinRanks; ++j) {
+      const uint32_t k = k0 + j;
+      uint32_t ak = k + (uint32_t)floor_div((uint64_t)Mp * H, total);
+      if (j < kWinRanks) A[k] = ak;
+      if (j == 0) a0 = ak;
+      if (bf16) {
+        uint32_t off = ak - a0;
+        if (off > 0xFFFFu) atomicOr(&narrow, 1);
+        a16[t * kWinEntries + j] = (uint16_t)off;
+      }
+      if (j < kWinRanks) H += hist[bf16 ? unrank_bf16(k) : unrank_e4m3(k)] + 1;
     }
-  if (t == 0) A[N] = N + Mp;
+    if (bf16) abase[t] = a0;
+  }
+  __syncthreads();
+  if (t == 0) {
+    A[N] = N + Mp;
+    if (bf16) abase[nwin] = N + Mp;
+    *aflag = bf16 && !narrow ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------- inverse CDF
+// For the decoder's first guess only (every decoded symbol is verified
+// exactly): u at y = m * MG / kNInv on the knot table's piecewise-linear CDF,
+// and the step to the next point.
+__global__ __launch_bounds__(1024) void k_uinv(const float2 *__restrict__ knots, float2 *__restrict__ uinv, uint32_t MG) {
+  __shared__ float U[kNInv + 1];
+  for (int m = threadIdx.x; m <= kNInv; m += blockDim.x) {
+    const double y = (double)m * (double)MG / (double)kNInv;
+    int lo = 0, hi = kNKnot - 1;  // largest i with K_i <= y, i < kNKnot - 1
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if ((double)knots[mid].x <= y) lo = mid; else hi = mid;
+    }
+    const float2 kd = knots[lo];
+    double u = (double)(lo - kUMax);
+    if (kd.y > 0.0f) u += ((y - (double)kd.x) / (double)kd.y);
+    U[m] = (float)fmin(fmax(u, -(double)kUMax), (double)kUMax);
+  }
+  __syncthreads();
+  for (int m = threadIdx.x; m <= kNInv; m += blockDim.x)
+    uinv[m] = make_float2(U[m], m < kNInv ? U[m + 1] - U[m] : 0.0f);
 }
 
 // ---------------------------------------------------------------- e4m3 bins
@@ -145,8 +199,9 @@ hipError_t launch_clear_status(int32_t *status, hipStream_t st) {
 hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, const Workspace &ws,
                         int32_t *status, hipStream_t st) {
   hipLaunchKernelGGL(k_knots, dim3(1), dim3(1024), 0, st, ws.knots, g.MG);
-  hipLaunchKernelGGL(k_ptable, dim3(1), dim3(1024), 0, st, hist, ws.ptab, g.N, g.Mp,
+  hipLaunchKernelGGL(k_ptable, dim3(1), dim3(1024), 0, st, hist, ws.ptab, ws.a16, ws.abase, ws.aflag, g.N, g.Mp,
                      g.sym_fmt == SKV_SYM_BF16 ? 1 : 0, status);
+  hipLaunchKernelGGL(k_uinv, dim3(1), dim3(1024), 0, st, ws.knots, ws.uinv, g.MG);
   if (g.sym_fmt == SKV_SYM_E4M3) hipLaunchKernelGGL(k_etab, dim3(1), dim3(256), 0, st, ws.etab);
   int64_t nch = g.rows * g.D;
   hipLaunchKernelGGL(k_scale, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, sigma, ws.scale, nch, status);

@@ -1,0 +1,121 @@
+// skv_modeldev.hpp -- the integer frequency model as device code, shared by the
+// encoder and the decoder so that both take every integer decision the same way.
+//
+// cum_lo(b) = A(rank b) + Cg(u(lo(b))), cum_hi(b) = A(rank b + 1) + Cg(u(hi(b))):
+// the mixture q ("Speculative KV coding", "早期结果") integrated over the bin of
+// b, in counts, with one count per symbol as a floor.
+#pragma once
+
+#include "skv_internal.hpp"
+
+namespace skv {
+
+// exact 48-bit product of two values below 2^24: v_mul_u32_u24 + v_mul_hi_u32_u24
+__device__ __forceinline__ uint64_t mul24(uint32_t a, uint32_t b) {
+  __builtin_assume(a < (1u << 24));
+  __builtin_assume(b < (1u << 24));
+  return (uint64_t)a * (uint64_t)b;
+}
+
+// Where the p_hat table A lives for a kernel.
+enum { kTabGlobal = 0,   // A from global memory only (the 16-bit window image does not fit)
+       kTabLdsAll = 1,   // all 1024 bf16 windows in LDS
+       kTabLdsWin = 2 }; // LDS holds windows [w0, w0 + nw); others from global memory
+
+struct ModelTabs {
+  const float2 *kn;      // LDS: knots (K_j, D_j)
+  const uint16_t *a16;   // LDS: window image, first window w0
+  const uint32_t *ab;    // LDS: window bases, first window w0 (e4m3: the full table A)
+  const uint32_t *ptab;  // global: full table A
+  const float2 *et;      // LDS: e4m3 bins
+  uint32_t w0, nw;
+};
+
+template <int TAB>
+__device__ __forceinline__ void a_pair(const ModelTabs &t, uint32_t k, uint32_t &alo, uint32_t &ahi) {
+  if (TAB == kTabGlobal) {
+    alo = t.ptab[k];
+    ahi = t.ptab[k + 1];
+    return;
+  }
+  const uint32_t w = k >> 6;
+  if (TAB == kTabLdsAll) {
+    const uint32_t e = k + w;  // = 65 w + (k mod 64)
+    const uint32_t base = t.ab[w];
+    alo = base + t.a16[e];
+    ahi = base + t.a16[e + 1];
+    return;
+  }
+  const uint32_t wl = w - t.w0;
+  const bool out = wl >= t.nw;
+  const uint32_t wc = out ? 0u : wl;
+  const uint32_t e = 65u * wc + (k & 63u);
+  const uint32_t base = t.ab[wc];
+  alo = base + t.a16[e];
+  ahi = base + t.a16[e + 1];
+  if (__builtin_expect(__any(out), 0)) {
+    if (out) {
+      alo = t.ptab[k];
+      ahi = t.ptab[k + 1];
+    }
+  }
+}
+
+// A(k) alone (k <= N)
+template <int TAB>
+__device__ __forceinline__ uint32_t a_one(const ModelTabs &t, uint32_t k) {
+  if (TAB == kTabGlobal) return t.ptab[k];
+  const uint32_t w = k >> 6;
+  if (TAB == kTabLdsAll) return t.ab[w] + t.a16[k + w];
+  const uint32_t wl = w - t.w0;
+  if (wl >= t.nw) return t.ptab[k];
+  return t.ab[wl] + t.a16[65u * wl + (k & 63u)];
+}
+
+// cum_lo and cum_hi of symbol b in model units (bf16: total 2^24, e4m3: 2^16)
+template <int SYM, int TAB>
+__device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float m, float s, uint32_t &clo,
+                                           uint32_t &chi) {
+  if (SYM == SKV_SYM_BF16) {
+    // The bin of a finite non-zero b is [(b-1):8000, b:8000] in fp32 bits for
+    // b > 0 and the same pair swapped for b < 0; Cg is monotone, so the lower
+    // count is the min of the two.  +-0, +-inf and NaN take the general edges.
+    const uint32_t eA = (b << 16) | 0x8000u;
+    const uint32_t eB = eA - 0x10000u;
+    const uint32_t cA = cg_eval(t.kn, u_of(__uint_as_float(eA), m, s));
+    const uint32_t cB = cg_eval(t.kn, u_of(__uint_as_float(eB), m, s));
+    uint32_t glo = min(cA, cB), ghi = max(cA, cB);
+    const bool special = ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17);
+    if (__builtin_expect(__any(special), 0)) {
+      if (special) {
+        float lo, hi;
+        bf16_bin(b, lo, hi);
+        glo = cg_eval(t.kn, u_of(lo, m, s));
+        ghi = cg_eval(t.kn, u_of(hi, m, s));
+      }
+    }
+    uint32_t alo, ahi;
+    a_pair<TAB>(t, rank_bf16(b), alo, ahi);
+    clo = alo + glo;
+    chi = ahi + ghi;
+  } else {
+    const float2 e = t.et[b];
+    const uint32_t k = rank_e4m3(b);
+    clo = t.ab[k] + cg_eval(t.kn, u_of(e.x, m, s));
+    chi = t.ab[k + 1] + cg_eval(t.kn, u_of(e.y, m, s));
+  }
+}
+
+// cum(k) = cum_lo(unrank k) for 0 <= k < N, cum(N) = T (decoder probes)
+template <int SYM, int TAB>
+__device__ __forceinline__ uint32_t cum_rank(const ModelTabs &t, uint32_t k, float m, float s) {
+  if (SYM == SKV_SYM_BF16) {
+    if (k >= 65536u) return 1u << 24;
+    return a_one<TAB>(t, k) + cg_eval(t.kn, u_of(bf16_lo_edge(unrank_bf16(k)), m, s));
+  } else {
+    if (k >= 256u) return 1u << 16;
+    return t.ab[k] + cg_eval(t.kn, u_of(t.et[unrank_e4m3(k)].x, m, s));
+  }
+}
+
+}  // namespace skv

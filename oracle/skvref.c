@@ -228,7 +228,7 @@ uint32_t skvref_cg(const ref_model *m, float u) {
 /* The empirical component p_hat: "the empirical bf16 symbol distribution   */
 /* measured on training data" ([SKV] "早期结果"), +1 smoothed.  Its integer */
 /* CDF in rank order: H(0) = 0, H(k+1) = H(k) + hist[unrank(k)] + 1,        */
-/* Qhat(k) = floor(Mp * H(k) / H(N)) (exact integers; needs Mp*H(N) < 2^64). */
+/* Qhat(k) = floor(Mp * H(k) / H(N)) (exact integers; domain Mp*H(N) < 2^62). */
 /* The table stored is A(k) = k + Qhat(k): the "+k" term is the floor of    */
 /* one count per symbol that keeps every frequency >= 1.                    */
 /* ------------------------------------------------------------------------ */
@@ -239,7 +239,7 @@ static int build_ptable(ref_model *m, const uint64_t *hist) {
     if (Htot + h + 1 < Htot) return REF_ERR_TABLE;
     Htot += h + 1;
   }
-  if (m->Mp != 0 && Htot > UINT64_MAX / m->Mp) return REF_ERR_TABLE;
+  if (m->Mp != 0 && Htot > (1ull << 62) / m->Mp) return REF_ERR_TABLE;
   uint64_t H = 0;
   for (uint32_t k = 0; k < m->N; k++) {
     m->A[k] = k + (uint32_t)((uint64_t)m->Mp * H / Htot);
