@@ -1,9 +1,8 @@
 // skv_decode.hip -- decode a range-coded KV cache on gfx950.
 //
 // Persistent grid, one 1024-thread block per CU with the model's tables in
-// LDS (knots, the inverse of the Gaussian pair's CDF, and the bf16 p_hat table
-// for ranks 8192..57343, i.e. every value below 2^64 in magnitude; rarer ranks
-// read the global copy).  Each wavefront decodes whole chunks; lane l decodes
+// LDS (knots 16 KB, the inverse of the Gaussian pair's CDF 8 KB, the bf16 p_hat
+// table 137 KB).  Each wavefront decodes whole chunks; lane l decodes
 // substream l, i.e. the same 8-scalar groups the encoder gave it, so one wave
 // step stores 1 KB of decoded bf16 contiguously.  The model is rebuilt from
 // (mu, sigma, hist), as both ends of the coder do ("Speculative KV coding",
@@ -13,17 +12,15 @@
 // r * cum_lo(s) <= d < r * cum_hi(s).  A guess comes from inverting the
 // Gaussian pair's CDF at t ~ d / r (fp32, approximate on purpose); the guess
 // is then verified with the exact integer model and the exact 48-bit
-// products, and a miss is corrected by a galloping search over ranks.  Any
-// exact search returns the same symbol, so the output does not depend on the
-// guess.
+// products.  A miss takes one secant step in rank space from the guess's exact
+// counts, then, if needed, a galloping search over ranks.  Any exact search
+// returns the same symbol, so the output does not depend on the guess.
 #include "skv_modeldev.hpp"
 
 namespace skv {
 
 constexpr int kDecBlock = 1024;
 constexpr int kDecWaves = kDecBlock / 64;
-constexpr uint32_t kDecW0 = 128;  // first LDS window: rank 8192
-constexpr uint32_t kDecNW = 768;  // windows in LDS: ranks 8192 .. 57343
 
 struct DecArgs {
   Geo g;
@@ -99,14 +96,11 @@ __device__ __forceinline__ uint32_t e4m3_guess(float e) {
   return sgn | min(code, 0x7Eu);
 }
 
-// A(k) for a guess: the LDS window clamps k (an approximate value is enough)
+// A(k) for a guess
 template <int SYM, int TAB>
 __device__ __forceinline__ uint32_t a_guess(const ModelTabs &t, uint32_t k) {
   if (SYM != SKV_SYM_BF16) return t.ab[k];
-  if (TAB == kTabGlobal) return t.ptab[k];
-  const uint32_t kc = min(max(k, 64u * kDecW0), 64u * (kDecW0 + kDecNW) - 1u);
-  const uint32_t wl = (kc >> 6) - kDecW0;
-  return t.ab[wl] + t.a16[65u * wl + (kc & 63u)];
+  return a_one<TAB>(t, k);
 }
 
 // The symbol whose bin holds the value where the Gaussian pair's CDF reaches
@@ -146,20 +140,22 @@ struct MuGroup {
   }
 };
 
-// The exact rank: largest k with r * (cum(k) << up) <= d, bracketed from the
-// guess kg (below: the answer is under kg; otherwise it is above kg).
+// The exact rank: the largest k with r * (cum(k) << up) <= d.  Known so far:
+// that holds at lo and fails at hi (hi = N: no bound), and the rank k0 was
+// probed: it holds (below = false) or fails (below = true) there.  Gallop away
+// from k0 towards the answer, then bisect.
 template <int SYM, int TAB>
-__device__ uint32_t search_rank(const ModelTabs &t, uint32_t kg, bool below, uint64_t d, uint32_t r, int up,
-                                float m, float s) {
+__device__ uint32_t search_rank(const ModelTabs &t, uint32_t k0, bool below, uint32_t lo, uint32_t hi, uint64_t d,
+                                uint32_t r, int up, float m, float s) {
   const uint32_t N = SYM == SKV_SYM_BF16 ? 65536u : 256u;
   auto leq = [&](uint32_t k) -> bool { return mul24(r, cum_rank<SYM, TAB>(t, k, m, s) << up) <= d; };
-  uint32_t lo, hi;
   if (below) {
-    hi = kg;
+    hi = min(hi, k0);
     uint32_t step = 1;
-    for (;;) {
-      const uint32_t p = hi > step ? hi - step : 0u;
-      if (p == 0 || leq(p)) {
+    while (hi - lo > 1) {
+      const uint32_t p = hi - lo > step ? hi - step : lo;
+      if (p == lo) break;
+      if (leq(p)) {
         lo = p;
         break;
       }
@@ -167,13 +163,11 @@ __device__ uint32_t search_rank(const ModelTabs &t, uint32_t kg, bool below, uin
       step <<= 1;
     }
   } else {
-    lo = kg + 1;
-    hi = N;
-    if (lo >= N) return N - 1;  // beyond the last symbol: a corrupt stream
+    lo = max(lo, k0);
     uint32_t step = 1;
-    for (;;) {
-      const uint32_t p = lo + step;
-      if (p >= N) break;
+    while (hi - lo > 1) {
+      const uint32_t p = hi - lo > step ? lo + step : hi;
+      if (p == hi || p >= N) break;
       if (leq(p)) {
         lo = p;
         step <<= 1;
@@ -184,16 +178,33 @@ __device__ uint32_t search_rank(const ModelTabs &t, uint32_t kg, bool below, uin
     }
   }
   while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) >> 1;
+    const uint32_t mid = lo + ((hi - lo) >> 1);
     if (leq(mid)) lo = mid; else hi = mid;
   }
   return lo;
+}
+
+// verify symbol g: d - r*cum_lo and whether it lies in [0, r*freq)
+template <int SYM, int TAB>
+__device__ __forceinline__ bool verify(const ModelTabs &t, uint32_t g, float m, float s, uint64_t d, uint32_t r,
+                                       int up, uint32_t &clo, uint32_t &chi, uint64_t &dd, uint64_t &pf,
+                                       bool &below) {
+  model_pair<SYM, TAB>(t, g, m, s, clo, chi);
+  const uint64_t plo = mul24(r, clo << up);
+  pf = mul24(r, (chi - clo) << up);
+  unsigned int b0, b1;
+  const uint32_t dl = __builtin_subc((uint32_t)d, (uint32_t)plo, 0u, &b0);
+  const uint32_t dh = __builtin_subc((uint32_t)(d >> 32), (uint32_t)(plo >> 32), b0, &b1);
+  dd = ((uint64_t)dh << 32) | dl;
+  below = b1 != 0;
+  return !below && dd < pf;
 }
 
 template <int SYM, int MU, int TAB>
 __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs &t, const float2 *uinv) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   constexpr int up = BF ? 0 : 8;
+  constexpr uint32_t N = BF ? 65536u : 256u;
   const Geo &g = a.g;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -264,30 +275,37 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
         gs = guess_symbol<SYM, TAB>(t, uinv, tq, BF ? rank_bf16(gs) : rank_e4m3(gs), a.inv_step, sinv[j], m);
         // ---- verify exactly
         uint32_t clo, chi;
-        model_pair<SYM, TAB>(t, gs, m, sj, clo, chi);
-        uint64_t plo = mul24(r, clo << up), pf = mul24(r, (chi - clo) << up);
-        unsigned int b0, b1;
-        uint32_t dl = __builtin_subc((uint32_t)d, (uint32_t)plo, 0u, &b0);
-        uint32_t dh = __builtin_subc((uint32_t)(d >> 32), (uint32_t)(plo >> 32), b0, &b1);
-        uint64_t dd = ((uint64_t)dh << 32) | dl;
-        bool ok = b1 == 0 && dd < pf;
+        uint64_t dd, pf;
+        bool below;
+        const bool ok = verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below);
         if (__builtin_expect(__any(!ok), 0)) {
           if (!ok) {
+            // one secant step in rank space on the guess's exact counts
             const uint32_t kg = BF ? rank_bf16(gs) : rank_e4m3(gs);
-            const uint32_t ks = search_rank<SYM, TAB>(t, kg, b1 != 0, d, r, up, m, sj);
-            gs = BF ? unrank_bf16(ks) : unrank_e4m3(ks);
-            model_pair<SYM, TAB>(t, gs, m, sj, clo, chi);
-            plo = mul24(r, clo << up);
-            pf = mul24(r, (chi - clo) << up);
-            dd = d - plo;
-            if (d < plo || dd >= pf) {  // no symbol holds d: corrupt stream
-              corrupt = true;
+            const float st = (tq - (float)clo) * __builtin_amdgcn_rcpf((float)(chi - clo));
+            int step = (int)__builtin_floorf(__builtin_fminf(__builtin_fmaxf(st, -70000.0f), 70000.0f));
+            step = below ? min(step, -1) : max(step, 1);
+            const int k2 = min(max((int)kg + step, 0), (int)N - 1);
+            uint32_t lo = below ? 0u : kg + 1, hi = below ? kg : N;  // holds at lo, fails at hi
+            if (lo < hi && (uint32_t)k2 >= lo && (uint32_t)k2 < hi) {
+              gs = BF ? unrank_bf16((uint32_t)k2) : unrank_e4m3((uint32_t)k2);
+              bool below2;
+              if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
+                const uint32_t ks = search_rank<SYM, TAB>(t, (uint32_t)k2, below2, lo, hi, d, r, up, m, sj);
+                gs = BF ? unrank_bf16(ks) : unrank_e4m3(ks);
+                if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
+                  corrupt = true;  // no symbol holds d
+                  dd = 0;
+                }
+              }
+            } else {
+              corrupt = true;  // d beyond the last symbol
               dd = 0;
             }
           }
         }
         // ---- update and renormalise
-        const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & ~7u;
+        const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & ~7u;  // pf >= r >= 2^16
         br.ensure(n8);
         d = (dd << n8) | br.take(n8);
         range = pf << n8;
@@ -320,8 +338,8 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   __shared__ float2 s_kn[kNKnot];
   __shared__ float2 s_ui[kNInv + 1];
-  __shared__ uint32_t s_a16w[BF ? kDecNW * kWinEntries / 2 : 1];
-  __shared__ uint32_t s_ab[BF ? kDecNW + 1 : 257];
+  __shared__ uint32_t s_a16w[BF ? kNWin * kWinEntries / 2 : 1];
+  __shared__ uint32_t s_ab[BF ? kNWin + 1 : 257];
   __shared__ float2 s_et[BF ? 1 : 256];
 
   const bool win = BF ? *a.aflag != 0 : true;
@@ -329,18 +347,17 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   for (int i = threadIdx.x; i <= kNInv; i += kDecBlock) s_ui[i] = a.uinv[i];
   if (BF) {
     if (win) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.a16 + kDecW0 * kWinEntries);
-      for (int i = threadIdx.x; i < (int)(kDecNW * kWinEntries / 2); i += kDecBlock) s_a16w[i] = src[i];
-      for (int i = threadIdx.x; i <= (int)kDecNW; i += kDecBlock) s_ab[i] = a.abase[kDecW0 + i];
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.a16);
+      for (int i = threadIdx.x; i < kNWin * kWinEntries / 2; i += kDecBlock) s_a16w[i] = src[i];
+      for (int i = threadIdx.x; i <= kNWin; i += kDecBlock) s_ab[i] = a.abase[i];
     }
   } else {
     for (int i = threadIdx.x; i < 257; i += kDecBlock) s_ab[i] = a.ptab[i];
     for (int i = threadIdx.x; i < 256; i += kDecBlock) s_et[i] = a.etab[i];
   }
   __syncthreads();
-  const ModelTabs t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, a.ptab, s_et, kDecW0, kDecNW};
-  if (!BF) decode_chunks<SYM, MU, kTabLdsAll>(a, t, s_ui);
-  else if (win) decode_chunks<SYM, MU, kTabLdsWin>(a, t, s_ui);
+  const ModelTabs t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, a.ptab, s_et, 0u, kNWin};
+  if (!BF || win) decode_chunks<SYM, MU, kTabLdsAll>(a, t, s_ui);
   else decode_chunks<SYM, MU, kTabGlobal>(a, t, s_ui);
 }
 

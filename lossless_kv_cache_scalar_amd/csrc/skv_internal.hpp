@@ -31,7 +31,7 @@ constexpr int kWinRanks = 64;
 constexpr int kWinEntries = kWinRanks + 1;
 constexpr int kNWin = 65536 / kWinRanks;
 // inverse of the Gaussian-pair CDF (counts -> knot coordinate), decoder guesses
-constexpr int kNInv = 2048;
+constexpr int kNInv = 1024;
 constexpr uint64_t kW48 = 0xFFFFFFFFFFFFull;
 constexpr uint64_t kTop40 = 1ull << 40;
 
