@@ -168,6 +168,32 @@ int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bits_bytes,
                const uint64_t *offsets, const void *mu, const float *sigma, const uint64_t *hist,
                void *x_out, void *workspace, size_t workspace_bytes, int32_t *status, void *stream);
 
+/* ---------------------------------------------------------------- kernel timing */
+
+/*
+ * Measurement aid, not part of the method.  Between skv_timing_start and
+ * skv_timing_stop every main launch of skv_encode / skv_decode (the model
+ * build as one record, k_encode, k_offsets, k_compact, k_decode) is bracketed
+ * by two HIP events recorded on the call's own stream, so one kernel's time is
+ * known without a profiler and without synchronising between calls.
+ * Recording is process-wide and meant for one host thread issuing the calls.
+ *
+ * skv_timing_start: creates 2 * capacity events on the current device
+ *   (1 <= capacity <= 2^20).  SKV_ERR_ARG if recording is already on or the
+ *   capacity is out of range, SKV_ERR_HIP if the events cannot be created.
+ *   Launches past the capacity go unrecorded.
+ * skv_timing_stop: waits for the recorded events, writes the first
+ *   min(count, capacity) records (host arrays: kernel id, milliseconds) in
+ *   launch order, stores the number recorded in *count (host), releases the
+ *   events and stops recording.  SKV_ERR_ARG if recording is off or a pointer
+ *   is null; SKV_ERR_HIP if an event could not be read (its time is 0).
+ * skv_timed_kernel_name: the name of a kernel id ("model", "k_encode",
+ *   "k_offsets", "k_compact", "k_decode"; "unknown" otherwise), static storage.
+ */
+int skv_timing_start(int32_t capacity);
+int skv_timing_stop(int32_t *kernel, float *ms, int32_t capacity, int32_t *count);
+const char *skv_timed_kernel_name(int32_t kernel);
+
 #ifdef __cplusplus
 }
 #endif

@@ -384,6 +384,7 @@ hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes,
                          const void *mu, const Workspace &ws, void *x_out, int32_t *status, hipStream_t st) {
   DecArgs a{g, bits, bits_bytes, offsets, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.uinv, ws.etab,
             ws.scale, (float)kNInv / (float)g.MG, x_out, status};
+  timing_mark(kTimeDecode, false, st);
   if (g.sym_fmt == SKV_SYM_BF16) {
     if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_BF16, SKV_MU_BF16>(a, st);
     else launch_dec_kernel<SKV_SYM_BF16, SKV_MU_F32>(a, st);
@@ -391,6 +392,7 @@ hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes,
     if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_E4M3, SKV_MU_BF16>(a, st);
     else launch_dec_kernel<SKV_SYM_E4M3, SKV_MU_F32>(a, st);
   }
+  timing_mark(kTimeDecode, true, st);
   return hipGetLastError();
 }
 

@@ -388,6 +388,7 @@ hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Work
                          uint64_t bits_cap, uint64_t *offsets, int32_t *status, hipStream_t st) {
   EncArgs a{g, x, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.etab, ws.scale, ws.lens, ws.sizes,
             ws.scratch, status};
+  timing_mark(kTimeEncode, false, st);
   if (g.sym_fmt == SKV_SYM_BF16) {
     if (g.mu_fmt == SKV_MU_BF16) launch_enc_kernel<SKV_SYM_BF16, SKV_MU_BF16>(a, st);
     else launch_enc_kernel<SKV_SYM_BF16, SKV_MU_F32>(a, st);
@@ -395,9 +396,14 @@ hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Work
     if (g.mu_fmt == SKV_MU_BF16) launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_BF16>(a, st);
     else launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_F32>(a, st);
   }
+  timing_mark(kTimeEncode, true, st);
+  timing_mark(kTimeOffsets, false, st);
   hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, st, ws.sizes, offsets, g.n_chunks, bits_cap, status);
+  timing_mark(kTimeOffsets, true, st);
+  timing_mark(kTimeCompact, false, st);
   hipLaunchKernelGGL(k_compact, dim3((unsigned)g.n_chunks), dim3(256), 0, st, ws.lens, ws.scratch, offsets, bits,
                      bits_cap, g.lane_cap);
+  timing_mark(kTimeCompact, true, st);
   return hipGetLastError();
 }
 

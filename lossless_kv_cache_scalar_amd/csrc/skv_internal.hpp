@@ -48,6 +48,12 @@ struct Geo {
   uint32_t lane_cap; // encoder scratch bytes per lane (multiple of 4)
 };
 
+// Optional per-kernel timing (skv_timing_start .. skv_timing_stop): while it
+// is on, timing_mark records a HIP event on `st` before (end = false) and after
+// (end = true) each main launch.
+enum TimedKernel { kTimeModel = 0, kTimeEncode, kTimeOffsets, kTimeCompact, kTimeDecode, kTimeCount };
+void timing_mark(int kernel, bool end, hipStream_t st);
+
 // ---- workspace layout (encode and decode share it) ----
 struct Workspace {
   float2 *knots;      // kNKnot (K_j, K_{j+1} - K_j)

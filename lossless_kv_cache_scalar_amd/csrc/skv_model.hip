@@ -198,6 +198,7 @@ hipError_t launch_clear_status(int32_t *status, hipStream_t st) {
 
 hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, const Workspace &ws,
                         int32_t *status, hipStream_t st) {
+  timing_mark(kTimeModel, false, st);
   hipLaunchKernelGGL(k_knots, dim3(1), dim3(1024), 0, st, ws.knots, g.MG);
   hipLaunchKernelGGL(k_ptable, dim3(1), dim3(1024), 0, st, hist, ws.ptab, ws.a16, ws.abase, ws.aflag, g.N, g.Mp,
                      g.sym_fmt == SKV_SYM_BF16 ? 1 : 0, status);
@@ -205,6 +206,7 @@ hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, 
   if (g.sym_fmt == SKV_SYM_E4M3) hipLaunchKernelGGL(k_etab, dim3(1), dim3(256), 0, st, ws.etab);
   int64_t nch = g.rows * g.D;
   hipLaunchKernelGGL(k_scale, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, sigma, ws.scale, nch, status);
+  timing_mark(kTimeModel, true, st);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ MU_BF16, MU_F32 = 0, 1
 # every function skv.h declares, in declaration order
 EXPORTS = ["skv_status_string", "skv_num_chunks", "skv_encode_bound", "skv_workspace_size",
            "skv_calib_state_size", "skv_calib_reset", "skv_calib_accumulate", "skv_calib_finalize",
-           "skv_calibrate", "skv_encode", "skv_decode"]
+           "skv_calibrate", "skv_encode", "skv_decode", "skv_timing_start", "skv_timing_stop",
+           "skv_timed_kernel_name"]
 
 
 class SkvShape(C.Structure):
@@ -59,8 +60,12 @@ def load():
     L.skv_calibrate.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp]
     L.skv_encode.argtypes = [sp, vp, vp, vp, vp, vp, sz, vp, vp, sz, i32p, vp]
     L.skv_decode.argtypes = [sp, vp, sz, vp, vp, vp, vp, vp, vp, sz, i32p, vp]
+    L.skv_timing_start.argtypes = [C.c_int32]
+    L.skv_timing_stop.argtypes = [C.POINTER(C.c_int32), C.POINTER(C.c_float), C.c_int32, C.POINTER(C.c_int32)]
+    L.skv_timed_kernel_name.argtypes = [C.c_int32]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = C.c_int
+    L.skv_timed_kernel_name.restype = C.c_char_p
     _lib = L
     return L
 
@@ -172,6 +177,21 @@ class Buffers:
 
     def stream_bytes(self) -> int:
         return int(self.offsets[-1].item())
+
+
+def timing_start(capacity: int) -> None:
+    """Start recording per-kernel HIP-event timings of the library's launches."""
+    _check(load().skv_timing_start(int(capacity)), "skv_timing_start")
+
+
+def timing_stop(capacity: int = 1 << 16):
+    """Stop recording; [(kernel name, ms), ...] in launch order."""
+    L = load()
+    ids = (C.c_int32 * capacity)()
+    ms = (C.c_float * capacity)()
+    n = C.c_int32(0)
+    _check(L.skv_timing_stop(ids, ms, int(capacity), C.byref(n)), "skv_timing_stop")
+    return [(L.skv_timed_kernel_name(ids[i]).decode(), float(ms[i])) for i in range(min(n.value, capacity))]
 
 
 def calibrate_sequences(seq_shape: SkvShape, seqs, device="cuda", stream=None):

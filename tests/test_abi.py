@@ -64,3 +64,14 @@ def test_null_pointers_rejected(lib):
     sh = skv.shape(1, 2, 256, 64)
     assert skv.encode(sh, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, stream=0) == skv.ERR_ARG
     assert skv.decode(sh, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, stream=0) == skv.ERR_ARG
+
+
+def test_timing_argument_checks(lib):
+    import ctypes as C
+    n = C.c_int32(-1)
+    assert lib.skv_timing_start(0) == skv.ERR_ARG
+    assert lib.skv_timing_start((1 << 20) + 1) == skv.ERR_ARG
+    assert lib.skv_timing_stop(None, None, 0, C.byref(n)) == skv.ERR_ARG  # not recording
+    assert lib.skv_timing_stop(None, None, 4, C.byref(n)) == skv.ERR_ARG
+    names = [skv.load().skv_timed_kernel_name(i).decode() for i in range(6)]
+    assert names == ["model", "k_encode", "k_offsets", "k_compact", "k_decode", "unknown"]

@@ -181,3 +181,18 @@ def test_encode_is_deterministic():
     torch.cuda.synchronize()
     n = a.stream_bytes()
     assert n == b.stream_bytes() and torch.equal(a.bits[:n], b.bits[:n]) and torch.equal(a.offsets, b.offsets)
+
+
+def test_kernel_timing_records_each_launch():
+    w, sh, x, mu, sigma, hist = _tiny_inputs()
+    buf = skv.Buffers(sh, device=DEV)
+    out = torch.empty_like(x)
+    skv.timing_start(16)
+    buf.encode(x, mu, sigma, hist)
+    buf.decode(mu, sigma, hist, out)
+    rec = skv.timing_stop(16)
+    assert [k for k, _ in rec] == ["model", "k_encode", "k_offsets", "k_compact", "model", "k_decode"]
+    assert all(ms > 0 for _, ms in rec)
+    assert torch.equal(out, x)
+    buf.encode(x, mu, sigma, hist)  # recording is off again: nothing recorded, nothing breaks
+    torch.cuda.synchronize()
