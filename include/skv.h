@@ -14,11 +14,17 @@
  * results: the mixture, sigma per (kv, head, channel)), "原生 FP8 KV 缓存"
  * (native FP8 cache: bin-integrated model over e4m3 symbols).
  *
- * The integer model, the range coder and the stream layout (chunks of one
- * (layer, kv, head) row x 256 tokens, 64 interleaved lane substreams, a u16
- * length header, u64 chunk offsets) are specified in the design notes that
- * ship with the library; the encoder output is a deterministic function of the
- * inputs, byte for byte.
+ * Stream layout.  A chunk is one (layer, kv, head) row's block of 256 tokens
+ * (the last block of a row may be shorter); chunk ids run over rows, then
+ * blocks.  Scalar i of a chunk (memory order, i = token * head_dim + channel)
+ * goes to lane i mod 64, and each of the 64 lanes range-codes its scalars in
+ * order as one substream (48-bit window, byte renormalisation, frequencies on a
+ * 2^24 total).  Chunk bytes: 64 little-endian u16 substream lengths; then, with
+ * m the fewest whole 4-byte words any substream has, words 0 .. m-1 of the 64
+ * substreams interleaved word by word (word w of lane l at 4 (64 w + l)); then
+ * the rest of each substream, lane by lane; then zeros up to a multiple of 4
+ * bytes.  u64 offsets[c] .. offsets[c+1] delimit chunk c.  The encoder output
+ * is a deterministic function of the inputs, byte for byte.
  *
  * Conventions for every entry point
  *   - Pointers marked (device) are device (HBM) pointers on the current HIP
@@ -80,8 +86,9 @@ const char *skv_status_string(int status);
  * SKV_ERR_UNSUPPORTED for a bad shape. */
 int skv_num_chunks(const skv_shape *shape, int64_t *n_chunks);
 
-/* Largest possible encoded size in bytes: n_chunks * (128 + 64) + 3 * n_scalars
- * (a frequency of 1 in 2^24 costs at most 3 bytes; one flush byte per lane). */
+/* Largest possible encoded size in bytes: n_chunks * (128 + 64 + 3) + 3 * n_scalars
+ * (a frequency of 1 in 2^24 costs at most 3 bytes; one flush byte per lane; at
+ * most 3 bytes of padding per chunk). */
 int skv_encode_bound(const skv_shape *shape, size_t *bytes);
 
 /* Device workspace needed by skv_encode and skv_decode for this shape. */

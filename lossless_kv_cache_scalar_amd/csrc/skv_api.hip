@@ -30,7 +30,9 @@ int make_geo(const skv_shape *sh, Geo &g) {
   if (sh->layers < 1 || sh->kv_heads < 1 || sh->tokens < 1 || sh->head_dim < 1) return SKV_ERR_ARG;
   if (sh->sym_fmt != SKV_SYM_BF16 && sh->sym_fmt != SKV_SYM_E4M3) return SKV_ERR_ARG;
   if (sh->mu_fmt != SKV_MU_BF16 && sh->mu_fmt != SKV_MU_F32) return SKV_ERR_ARG;
-  if (sh->head_dim % kGroup != 0 || (kGroup * kLanes) % sh->head_dim != 0) return SKV_ERR_UNSUPPORTED;
+  // head_dim a power of two from 8 to 512: a lane's channels then repeat with
+  // a period dividing kBatch
+  if (sh->head_dim % 8 != 0 || 512 % sh->head_dim != 0) return SKV_ERR_UNSUPPORTED;
   if (sh->layers > (1 << 20) || sh->kv_heads > (1 << 16) || sh->tokens > (int64_t(1) << 32)) return SKV_ERR_ARG;
   g.layers = sh->layers;
   g.heads = sh->kv_heads;
@@ -67,7 +69,7 @@ Layout layout(const Geo &g) {
   L.aflag = o; o = align_up(o + sizeof(int32_t));
   L.uinv = o;  o = align_up(o + sizeof(float2) * (kNInv + 1));
   L.etab = o;  o = align_up(o + sizeof(float2) * 256);
-  L.scale = o; o = align_up(o + sizeof(float) * (size_t)(g.rows * g.D));
+  L.scale = o; o = align_up(o + sizeof(float2) * (size_t)(g.rows * g.D));
   L.lens = o;  o = align_up(o + sizeof(uint32_t) * (size_t)g.n_chunks * kLanes);
   L.sizes = o; o = align_up(o + sizeof(uint64_t) * (size_t)g.n_chunks);
   L.scratch = o; o = align_up(o + (size_t)g.n_chunks * kLanes * g.lane_cap);
@@ -86,7 +88,7 @@ Workspace carve(const Geo &g, void *base) {
   w.aflag = reinterpret_cast<int32_t *>(b + L.aflag);
   w.uinv = reinterpret_cast<float2 *>(b + L.uinv);
   w.etab = reinterpret_cast<float2 *>(b + L.etab);
-  w.scale = reinterpret_cast<float *>(b + L.scale);
+  w.scale = reinterpret_cast<float2 *>(b + L.scale);
   w.lens = reinterpret_cast<uint32_t *>(b + L.lens);
   w.sizes = reinterpret_cast<uint64_t *>(b + L.sizes);
   w.scratch = b + L.scratch;
@@ -114,7 +116,7 @@ extern "C" int skv_encode_bound(const skv_shape *shape, size_t *bytes) {
   if (e != SKV_OK) return e;
   if (!bytes) return SKV_ERR_ARG;
   size_t nsc = (size_t)(g.rows * g.tokens * g.D);
-  *bytes = (size_t)g.n_chunks * (kHeaderBytes + kLanes) + 3 * nsc;
+  *bytes = (size_t)g.n_chunks * (kHeaderBytes + kLanes + 3) + 3 * nsc;
   return SKV_OK;
 }
 

@@ -3,18 +3,22 @@
 // Persistent grid, one 1024-thread block per CU with the model's tables in
 // LDS (knots 16 KB, the inverse of the Gaussian pair's CDF 8 KB, the bf16 p_hat
 // table 137 KB).  Each wavefront decodes whole chunks; lane l decodes
-// substream l, i.e. the same 8-scalar groups the encoder gave it, so one wave
-// step stores 1 KB of decoded bf16 contiguously.  The model is rebuilt from
+// substream l, the chunk's scalars l, l + 64, ...  The model is rebuilt from
 // (mu, sigma, hist), as both ends of the coder do ("Speculative KV coding",
 // "什么能预测 KV 缓存").
 //
 // Symbol search.  The decoder needs the unique symbol s with
 // r * cum_lo(s) <= d < r * cum_hi(s).  A guess comes from inverting the
-// Gaussian pair's CDF at t ~ d / r (fp32, approximate on purpose); the guess
-// is then verified with the exact integer model and the exact 48-bit
-// products.  A miss takes one secant step in rank space from the guess's exact
-// counts, then, if needed, a galloping search over ranks.  Any exact search
-// returns the same symbol, so the output does not depend on the guess.
+// Gaussian pair's CDF at t ~ d / r (fp32, approximate on purpose), twice: at
+// t - A(rank of mu), then at t - A(rank of the first guess).  The guess is
+// verified with the exact integer model and exact 48-bit products.  A miss
+// takes one secant step in rank space from the guess's exact counts, then, if
+// needed, a galloping search over ranks.  Any exact search returns the same
+// symbol, so the output does not depend on the guesses.
+//
+// Stream reads.  Word w of a lane is word 64 w + l of the chunk's interleaved
+// region while w < m, so the lanes' refills read 256 contiguous bytes; each
+// lane keeps its next word in flight.
 #include "skv_modeldev.hpp"
 
 namespace skv {
@@ -35,51 +39,69 @@ struct DecArgs {
   const int32_t *aflag;
   const float2 *uinv;
   const float2 *etab;
-  const float *scale;
+  const float2 *scale;
   float inv_step;  // kNInv / MG
   void *x_out;
   int32_t *status;
 };
 
-// Bits of one substream, most significant first; bytes past its end read as 0.
-struct BitReader {
-  const uint8_t *bits;
-  uint64_t ib;   // next bits, left-aligned
-  int nib;       // valid bits in ib
-  uint64_t wp;   // next aligned word to load
-  uint64_t end;  // substream end (exclusive)
+// Bits of one lane's substream, most significant first; bytes at or past its
+// length read as 0.  ib holds the bits before word w; the two aligned dwords
+// that hold word w are in flight in (plo, phi) from the moment word w - 1 is
+// taken until take() needs word w.
+struct LaneReader {
+  const uint8_t *chunk;  // chunk start, 4-byte aligned
+  uint32_t csize;        // chunk bytes (a multiple of 4, >= 192)
+  uint32_t m;            // interleaved words per lane
+  uint32_t lane, tail, len;
+  uint32_t w, plo, phi;
+  uint64_t ib;  // next bits, left-aligned
+  int nib;      // valid bits in ib
 
-  __device__ __forceinline__ void refill() {  // needs nib <= 32
-    uint32_t w = 0;
-    if (wp < end) {
-      w = __builtin_bswap32(*reinterpret_cast<const uint32_t *>(bits + wp));
-      const uint64_t valid = end - wp;
-      if (valid < 4) w &= ~(0xFFFFFFFFu >> (8 * (uint32_t)valid));
-    }
-    ib |= (uint64_t)w << (32 - nib);
-    nib += 32;
-    wp += 4;
+  // chunk byte offset of byte 4 wi of the lane
+  __device__ __forceinline__ uint32_t pos(uint32_t wi) const {
+    return wi < m ? kHeaderBytes + 4u * (wi * kLanes + lane) : tail + 4u * (wi - m);
   }
-  __device__ __forceinline__ void init(const uint8_t *b, uint64_t st, uint64_t e) {
-    bits = b;
-    end = e;
-    wp = st & ~3ull;
-    ib = 0;
-    nib = 0;
-    refill();
-    const int skip = 8 * (int)(st & 3);
-    ib <<= skip;
-    nib -= skip;
+  __device__ __forceinline__ void issue() {
+    const uint32_t p = pos(w);
+    uint32_t a0 = p & ~3u;
+    if (4u * w >= len) a0 = 0u;  // nothing left: any dword of the chunk, masked off below
+    uint32_t a1 = a0 + 4u;
+    if (a1 >= csize) a1 = a0;
+    plo = *reinterpret_cast<const uint32_t *>(chunk + a0);
+    phi = *reinterpret_cast<const uint32_t *>(chunk + a1);
   }
-  // n in {0, 8, 16, 24}, after ensure(n)
+  __device__ __forceinline__ uint32_t word() const {
+    const uint32_t sh = 8u * (pos(w) & 3u);
+    uint32_t v = __builtin_bswap32((uint32_t)((((uint64_t)phi << 32) | plo) >> sh));
+    const int valid = (int)len - 4 * (int)w;
+    if (valid <= 0) return 0u;
+    if (valid < 4) v &= ~(0xFFFFFFFFu >> (8 * valid));
+    return v;
+  }
+  __device__ __forceinline__ void init() {
+    w = 0;
+    issue();
+    ib = (uint64_t)word() << 32;
+    w = 1;
+    issue();
+    ib |= word();
+    nib = 64;
+    w = 2;
+    issue();
+  }
+  // n in {0, 8, 16, 24}
   __device__ __forceinline__ uint32_t take(uint32_t n) {
+    if (nib < (int)n) {  // nib <= 23
+      ib |= (uint64_t)word() << (32 - nib);
+      nib += 32;
+      ++w;
+      issue();
+    }
     const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)(ib >> 32), (0u - n) & 31u, n);
     ib <<= n;
     nib -= (int)n;
     return v;
-  }
-  __device__ __forceinline__ void ensure(uint32_t n) {
-    if (nib < (int)n) refill();
   }
 };
 
@@ -117,28 +139,6 @@ __device__ __forceinline__ uint32_t guess_symbol(const ModelTabs &t, const float
   const float e = __builtin_fmaf(uu, sinv, m);
   return SYM == SKV_SYM_BF16 ? bf16_rne_bits(e) : e4m3_guess(e);
 }
-
-template <int SYM, int MU>
-struct MuGroup {
-  uint4 v0, v1;
-  __device__ __forceinline__ void load(const void *mu, int64_t i0) {
-    if (MU == SKV_MU_BF16) {
-      v0 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(mu) + i0);
-    } else {
-      const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(mu) + i0);
-      v0 = p[0];
-      v1 = p[1];
-    }
-  }
-  __device__ __forceinline__ float get(int j) const {
-    if (MU == SKV_MU_BF16) {
-      const uint32_t w[4] = {v0.x, v0.y, v0.z, v0.w};
-      return mu_from_bf16((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    }
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    return mu_from_f32(__uint_as_float(w[j]));
-  }
-};
 
 // The exact rank: the largest k with r * (cum(k) << up) <= d.  Known so far:
 // that holds at lo and fails at hi (hi = N: no bound), and the rank k0 was
@@ -200,130 +200,173 @@ __device__ __forceinline__ bool verify(const ModelTabs &t, uint32_t g, float m, 
   return !below && dd < pf;
 }
 
+// A lane's next kBatch predictor means (symbols i0, i0 + 64, ...), raw.
+template <int MU>
+struct MuBatch {
+  uint32_t v[kBatch];
+  __device__ __forceinline__ uint32_t one(const void *mu, uint32_t i) const {
+    return MU == SKV_MU_BF16 ? (uint32_t) static_cast<const uint16_t *>(mu)[i] : static_cast<const uint32_t *>(mu)[i];
+  }
+  __device__ __forceinline__ void load_full(const void *mu, uint32_t i0) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = one(mu, i0 + kLanes * j);
+  }
+  __device__ __forceinline__ void load_part(const void *mu, uint32_t i0, int valid) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = j < valid ? one(mu, i0 + kLanes * j) : 0u;
+  }
+  __device__ __forceinline__ float get(int j) const {
+    return MU == SKV_MU_BF16 ? mu_from_bf16(v[j]) : mu_from_f32(__uint_as_float(v[j]));
+  }
+};
+
+// Decode one symbol of a lane: returns its pattern and advances the coder.
 template <int SYM, int MU, int TAB>
-__device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs &t, const float2 *uinv) {
+__device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelTabs &t, const float2 *uinv,
+                                                  LaneReader &br, uint64_t &d, uint64_t &range, uint32_t &shifted,
+                                                  bool &corrupt, float m, float sj, float sinvj) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   constexpr int up = BF ? 0 : 8;
   constexpr uint32_t N = BF ? 65536u : 256u;
+  const uint32_t r = (uint32_t)(range >> 24);
+  // ---- guess: invert the Gaussian pair's CDF at t - A(k), first with k the
+  // rank of mu, then with k the rank of that first guess (the one-count floor
+  // makes A(k) grow by one per rank, which matters near zero)
+  const float tq = (float)(uint32_t)(d >> 16) * (65536.0f * __builtin_amdgcn_rcpf((float)(r << up)));
+  uint32_t kmu;
+  if (BF) kmu = rank_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : (__float_as_uint(m) >> 16));
+  else kmu = rank_e4m3(e4m3_guess(m));
+  uint32_t gs = guess_symbol<SYM, TAB>(t, uinv, tq, kmu, a.inv_step, sinvj, m);
+  gs = guess_symbol<SYM, TAB>(t, uinv, tq, BF ? rank_bf16(gs) : rank_e4m3(gs), a.inv_step, sinvj, m);
+  // ---- verify exactly
+  uint32_t clo, chi;
+  uint64_t dd, pf;
+  bool below;
+  const bool ok = verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below);
+  if (__builtin_expect(__any(!ok), 0)) {
+    if (!ok) {
+      // one secant step in rank space on the guess's exact counts
+      const uint32_t kg = BF ? rank_bf16(gs) : rank_e4m3(gs);
+      const float st = (tq - (float)clo) * __builtin_amdgcn_rcpf((float)(chi - clo));
+      int step = (int)__builtin_floorf(__builtin_fminf(__builtin_fmaxf(st, -70000.0f), 70000.0f));
+      step = below ? min(step, -1) : max(step, 1);
+      const int k2 = min(max((int)kg + step, 0), (int)N - 1);
+      uint32_t lo = below ? 0u : kg + 1, hi = below ? kg : N;  // holds at lo, fails at hi
+      if (lo < hi && (uint32_t)k2 >= lo && (uint32_t)k2 < hi) {
+        gs = BF ? unrank_bf16((uint32_t)k2) : unrank_e4m3((uint32_t)k2);
+        bool below2;
+        if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
+          const uint32_t ks = search_rank<SYM, TAB>(t, (uint32_t)k2, below2, lo, hi, d, r, up, m, sj);
+          gs = BF ? unrank_bf16(ks) : unrank_e4m3(ks);
+          if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
+            corrupt = true;  // no symbol holds d
+            dd = 0;
+          }
+        }
+      } else {
+        corrupt = true;  // d beyond the last symbol
+        dd = 0;
+      }
+    }
+  }
+  // ---- update and renormalise
+  const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & ~7u;  // pf >= r >= 2^16
+  d = (dd << n8) | br.take(n8);
+  range = pf << n8;
+  shifted += n8 >> 3;
+  return gs;
+}
+
+template <int SYM, int MU, int TAB>
+__device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs &t, const float2 *uinv) {
+  constexpr bool BF = SYM == SKV_SYM_BF16;
   const Geo &g = a.g;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const uint32_t D = (uint32_t)g.D;
+  constexpr int kStep = kLanes * kBatch;  // scalars of one batch of the wave
   for (int64_t chunk = (int64_t)blockIdx.x * kDecWaves + wave; chunk < g.n_chunks;
        chunk += (int64_t)gridDim.x * kDecWaves) {
     const int64_t row = chunk / g.ntb, blk = chunk - row * g.ntb;
     const int64_t tok = min<int64_t>(kChunkTokens, g.tokens - blk * kChunkTokens);
-    const int ngroups = (int)(tok * g.D / kGroup);
+    const int nsc = (int)(tok * g.D);
     const int64_t base = (row * g.tokens + blk * kChunkTokens) * g.D;
 
-    // ---- header: lane lengths, their prefix, consistency with the offsets
+    // ---- header: lane lengths, the interleaved word count m, the tails' offsets
     const uint64_t o0 = a.offsets[chunk], o1 = a.offsets[chunk + 1];
     const uint64_t nbytes = o1 >= o0 ? o1 - o0 : 0;
-    bool corrupt = o1 < o0 || o1 > a.bits_bytes || nbytes < (uint64_t)kHeaderBytes;
-    uint32_t len = 0;
-    if (!corrupt) len = (uint32_t)a.bits[o0 + 2 * lane] | ((uint32_t)a.bits[o0 + 2 * lane + 1] << 8);
-    uint32_t pre = len;
+    bool corrupt = o1 < o0 || o1 > a.bits_bytes || nbytes < (uint64_t)kHeaderBytes || (o0 & 3u) != 0 ||
+                   nbytes > 0xFFFFFFFFull;
+    uint32_t len = corrupt ? 0u : (uint32_t) reinterpret_cast<const uint16_t *>(a.bits + o0)[lane];
+    uint32_t mw = len >> 2;
+    for (int off = 32; off > 0; off >>= 1) mw = min(mw, (uint32_t)__shfl_xor((int)mw, off, 64));
+    uint32_t inc = len - 4u * mw;
     for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(pre, off, 64);
-      if (lane >= off) pre += v;
+      const uint32_t v = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += v;
     }
-    const uint32_t total = __shfl(pre, 63, 64);
-    uint64_t start = (uint64_t)kHeaderBytes + (pre - len);
-    if (!corrupt && (uint64_t)kHeaderBytes + total != nbytes) corrupt = true;
+    const uint32_t tails = __shfl(inc, 63, 64);
+    const uint64_t total = (uint64_t)kHeaderBytes + 4ull * kLanes * mw + tails;  // = 128 + sum of lengths
+    if (!corrupt && ((total + 3) & ~3ull) != nbytes) corrupt = true;
     if (len == 0) corrupt = true;
-    if (corrupt) len = 0;  // a chunk outside the buffer reads nothing
-    if (start > nbytes) start = nbytes;
-    if (start + len > nbytes) len = (uint32_t)(nbytes - start);
-
-    const int d0 = (kGroup * lane) % (int)g.D;
-    float s[kGroup], sinv[kGroup];
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      s[j] = a.scale[row * g.D + d0 + j];
-      sinv[j] = __builtin_amdgcn_rcpf(s[j]);  // ~sigma / 64, guesses only
+    if (__any(corrupt)) {  // the whole chunk is flagged and nothing of it is read
+      set_status(a.status, SKV_ERR_CORRUPT);
+      continue;
     }
-
-    // a corrupt chunk reads nothing: its reader starts and ends at byte 0
-    const uint64_t st = corrupt ? 0 : o0 + start;
-    BitReader br;
-    br.init(a.bits, st, st + len);
-    br.ensure(24);
+    LaneReader br;
+    br.chunk = a.bits + o0;
+    br.csize = (uint32_t)nbytes;
+    br.m = mw;
+    br.lane = (uint32_t)lane;
+    br.tail = kHeaderBytes + 4u * kLanes * mw + inc - (len - 4u * mw);
+    br.len = len;
+    br.init();
     uint64_t d = (uint64_t)br.take(24) << 24;
-    br.ensure(24);
     d |= br.take(24);
     uint64_t range = kW48;
     uint32_t shifted = 0;  // renormalisation bytes consumed
 
-    MuGroup<SYM, MU> cur;
-    if (lane < ngroups) cur.load(a.mu, base + (int64_t)lane * kGroup);
-    for (int grp = lane; grp < ngroups; grp += kLanes) {
-      const int64_t i0 = base + (int64_t)grp * kGroup;
-      MuGroup<SYM, MU> nxt;
-      if (grp + kLanes < ngroups) nxt.load(a.mu, i0 + kLanes * kGroup);
-      uint32_t out[kGroup];
+    // ---- symbols: lane l decodes scalars l, l + 64, ... of the chunk; symbol
+    // k has channel (l + 64 k) mod D, which repeats with a period dividing kBatch
+    float s[kBatch], sinv[kBatch];
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        const float m = cur.get(j), sj = s[j];
-        const uint32_t r = (uint32_t)(range >> 24);
-        // ---- guess: invert the Gaussian pair's CDF at t - A(k), first with k the
-        // rank of mu, then with k the rank of that first guess (the one-count
-        // floor makes A(k) grow by one per rank, which matters near zero)
-        const float tq = (float)(uint32_t)(d >> 16) * (65536.0f * __builtin_amdgcn_rcpf((float)(r << up)));
-        uint32_t kmu;
-        if (BF) kmu = rank_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : (__float_as_uint(m) >> 16));
-        else kmu = rank_e4m3(e4m3_guess(m));
-        uint32_t gs = guess_symbol<SYM, TAB>(t, uinv, tq, kmu, a.inv_step, sinv[j], m);
-        gs = guess_symbol<SYM, TAB>(t, uinv, tq, BF ? rank_bf16(gs) : rank_e4m3(gs), a.inv_step, sinv[j], m);
-        // ---- verify exactly
-        uint32_t clo, chi;
-        uint64_t dd, pf;
-        bool below;
-        const bool ok = verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below);
-        if (__builtin_expect(__any(!ok), 0)) {
-          if (!ok) {
-            // one secant step in rank space on the guess's exact counts
-            const uint32_t kg = BF ? rank_bf16(gs) : rank_e4m3(gs);
-            const float st = (tq - (float)clo) * __builtin_amdgcn_rcpf((float)(chi - clo));
-            int step = (int)__builtin_floorf(__builtin_fminf(__builtin_fmaxf(st, -70000.0f), 70000.0f));
-            step = below ? min(step, -1) : max(step, 1);
-            const int k2 = min(max((int)kg + step, 0), (int)N - 1);
-            uint32_t lo = below ? 0u : kg + 1, hi = below ? kg : N;  // holds at lo, fails at hi
-            if (lo < hi && (uint32_t)k2 >= lo && (uint32_t)k2 < hi) {
-              gs = BF ? unrank_bf16((uint32_t)k2) : unrank_e4m3((uint32_t)k2);
-              bool below2;
-              if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
-                const uint32_t ks = search_rank<SYM, TAB>(t, (uint32_t)k2, below2, lo, hi, d, r, up, m, sj);
-                gs = BF ? unrank_bf16(ks) : unrank_e4m3(ks);
-                if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
-                  corrupt = true;  // no symbol holds d
-                  dd = 0;
-                }
-              }
-            } else {
-              corrupt = true;  // d beyond the last symbol
-              dd = 0;
-            }
+    for (int j = 0; j < kBatch; ++j) {
+      const float2 sc = a.scale[row * g.D + ((lane + kLanes * j) & (D - 1))];
+      s[j] = sc.x;
+      sinv[j] = sc.y;
+    }
+    const void *mu_ch = MU == SKV_MU_BF16 ? (const void *)(static_cast<const uint16_t *>(a.mu) + base)
+                                          : (const void *)(static_cast<const float *>(a.mu) + base);
+    void *x_ch = BF ? (void *)(static_cast<uint16_t *>(a.x_out) + base) : (void *)(static_cast<uint8_t *>(a.x_out) + base);
+    const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;
+    const int nfull = nsc / kStep;
+    const int nb = (nsc + kStep - 1) / kStep;
+    MuBatch<MU> cur, nxt;
+    if (nfull > 0) cur.load_full(mu_ch, lane);
+    else cur.load_part(mu_ch, lane, nk);
+    for (int b = 0; b < nb; ++b) {
+      const uint32_t i0 = (uint32_t)lane + (uint32_t)b * kStep;
+      if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
+      else if (b + 1 < nb) nxt.load_part(mu_ch, i0 + kStep, nk - (b + 1) * kBatch);
+      if (b < nfull) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, cur.get(j), s[j],
+                                                          sinv[j]);
+          if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
+          else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
+        }
+      } else {
+        const int v = nk - b * kBatch;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (j < v) {
+            const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, cur.get(j),
+                                                            s[j], sinv[j]);
+            if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
+            else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
           }
         }
-        // ---- update and renormalise
-        const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & ~7u;  // pf >= r >= 2^16
-        br.ensure(n8);
-        d = (dd << n8) | br.take(n8);
-        range = pf << n8;
-        shifted += n8 >> 3;
-        out[j] = gs;
-      }
-      if (BF) {
-        uint4 v;
-        v.x = out[0] | (out[1] << 16);
-        v.y = out[2] | (out[3] << 16);
-        v.z = out[4] | (out[5] << 16);
-        v.w = out[6] | (out[7] << 16);
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.x_out) + i0) = v;
-      } else {
-        uint2 v;
-        v.x = out[0] | (out[1] << 8) | (out[2] << 16) | (out[3] << 24);
-        v.y = out[4] | (out[5] << 8) | (out[6] << 16) | (out[7] << 24);
-        *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(a.x_out) + i0) = v;
       }
       cur = nxt;
     }

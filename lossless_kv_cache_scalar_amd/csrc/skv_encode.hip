@@ -3,14 +3,16 @@
 // Persistent grid, one 1024-thread block per CU: every table the model needs
 // lives in LDS (knots 16 KB; the bf16 p_hat table in its 64-rank-window u16
 // layout, 137 KB).  Each wavefront codes whole chunks (one (layer, kv, head)
-// row x 256 tokens); lane l codes the chunk's 8-scalar groups l, l + 64, ...
-// as its own substream.  A group of 8 bf16 symbols and its 8 predictor means
-// are one 16-byte load each, so a wave reads 1 KB of x and of mu per step.
+// row x 256 tokens); lane l codes the chunk's scalars l, l + 64, l + 128, ...
+// as its own substream, so one wave step reads 64 consecutive scalars of x and
+// of mu.  Lanes load their next 8 symbols while coding the current 8.
 //
-// Each lane writes its substream, as whole 32-bit words, to its own scratch
-// slot; a scan over chunk sizes gives the offsets and a compaction kernel
-// writes every chunk (u16 length header, then the 64 substreams) at its
-// offset with coalesced word stores.
+// Each lane writes its substream as whole 32-bit words into the chunk's
+// scratch slot, word w of lane l at word 64 w + l: a wave's stores land side
+// by side, and the first m words of every lane already sit in the stream's
+// interleaved layout.  A scan over chunk sizes gives the offsets; a compaction
+// kernel writes each chunk (length header, interleaved words, the lanes'
+// remaining bytes, padding) at its offset.
 #include "skv_internal.hpp"
 
 namespace skv {
@@ -27,7 +29,7 @@ struct EncArgs {
   const uint32_t *abase;
   const int32_t *aflag;
   const float2 *etab;
-  const float *scale;
+  const float2 *scale;
   uint32_t *lens;
   uint64_t *sizes;
   uint8_t *scratch;
@@ -42,7 +44,8 @@ __device__ __forceinline__ uint64_t mul24(uint32_t a, uint32_t b) {
 }
 
 // A carry that ran through all 16 pending bits of the coder register: add one
-// to the bits already emitted (the valid low nbits of acc, then stored words).
+// to the bits already emitted (the valid low nbits of acc, then stored words;
+// a lane's word w is out[64 w]).
 __device__ __noinline__ uint64_t carry_out(uint64_t acc, int nbits, uint32_t *out, uint32_t nw, uint32_t capw) {
   if (nbits > 0) {
     const uint64_t mask = (1ull << nbits) - 1ull;
@@ -51,8 +54,8 @@ __device__ __noinline__ uint64_t carry_out(uint64_t acc, int nbits, uint32_t *ou
     if (v != 0) return acc;
   }
   for (int w = (int)min(nw, capw) - 1; w >= 0; --w) {
-    const uint32_t v = __builtin_bswap32(out[w]) + 1u;
-    out[w] = __builtin_bswap32(v);
+    const uint32_t v = __builtin_bswap32(out[(uint32_t)w * kLanes]) + 1u;
+    out[(uint32_t)w * kLanes] = __builtin_bswap32(v);
     if (v != 0) break;
   }
   return acc;
@@ -62,7 +65,7 @@ __device__ __noinline__ uint64_t carry_out(uint64_t acc, int nbits, uint32_t *ou
 // the two most recently emitted bytes above it, so most carries resolve by
 // plain 64-bit addition; emitted bits collect in acc (nbits valid, the first
 // 16 bits shifted out of X are the empty pending bytes of the initial state)
-// and leave as whole words.
+// and leave as whole words, word w at out[64 w].
 struct LaneCoder {
   uint64_t X, range, acc;
   int nbits;
@@ -83,7 +86,7 @@ struct LaneCoder {
   __device__ __forceinline__ void flush_word() {
     if (nbits >= 32) {
       const uint32_t word = (uint32_t)(acc >> (nbits - 32));
-      out[min(nw, capw - 1)] = __builtin_bswap32(word);
+      out[min(nw, capw - 1) * kLanes] = __builtin_bswap32(word);
       ++nw;
       nbits -= 32;
     }
@@ -120,43 +123,37 @@ struct LaneCoder {
     acc = (acc << 24) | (X >> 40);
     nbits += 24;
     flush_word();
-    if (nbits > 0 && nw < capw) out[nw] = __builtin_bswap32((uint32_t)(acc << (32 - nbits)));
+    if (nbits > 0 && nw < capw) out[nw * kLanes] = __builtin_bswap32((uint32_t)(acc << (32 - nbits)));
     return 4u * nw + (uint32_t)nbits / 8u;
   }
 };
 
-// One group of 8 scalars as loaded: symbols and predictor means.
+// A lane's next kBatch symbols and predictor means (symbols i0, i0 + 64, ...).
 template <int SYM, int MU>
-struct Group {
-  uint4 xv;
-  uint4 mv0, mv1;  // mv1 only for fp32 means
-  __device__ __forceinline__ void load(const EncArgs &a, int64_t i0) {
-    if (SYM == SKV_SYM_BF16) {
-      xv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + i0);
-    } else {
-      const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint8_t *>(a.x) + i0);
-      xv = make_uint4(v.x, v.y, 0u, 0u);
-    }
-    if (MU == SKV_MU_BF16) {
-      mv0 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.mu) + i0);
-    } else {
-      const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.mu) + i0);
-      mv0 = p[0];
-      mv1 = p[1];
-    }
+struct Batch {
+  uint32_t xs[kBatch];
+  uint32_t ms[kBatch];  // bf16 pattern or fp32 bits
+  __device__ __forceinline__ void one(const EncArgs &a, int64_t i, int j) {
+    xs[j] = SYM == SKV_SYM_BF16 ? (uint32_t) static_cast<const uint16_t *>(a.x)[i]
+                                : (uint32_t) static_cast<const uint8_t *>(a.x)[i];
+    ms[j] = MU == SKV_MU_BF16 ? (uint32_t) static_cast<const uint16_t *>(a.mu)[i]
+                              : static_cast<const uint32_t *>(a.mu)[i];
   }
-  __device__ __forceinline__ uint32_t sym(int j) const {
-    const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
-    if (SYM == SKV_SYM_BF16) return (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    return (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+  __device__ __forceinline__ void load_full(const EncArgs &a, int64_t i0) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) one(a, i0 + (int64_t)kLanes * j, j);
+  }
+  // only the first `valid` symbols exist (valid may be <= 0)
+  __device__ __forceinline__ void load_part(const EncArgs &a, int64_t i0, int valid) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      xs[j] = 0;
+      ms[j] = 0;
+      if (j < valid) one(a, i0 + (int64_t)kLanes * j, j);
+    }
   }
   __device__ __forceinline__ float mu(int j) const {
-    if (MU == SKV_MU_BF16) {
-      const uint32_t w[4] = {mv0.x, mv0.y, mv0.z, mv0.w};
-      return mu_from_bf16((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    }
-    const uint32_t w[8] = {mv0.x, mv0.y, mv0.z, mv0.w, mv1.x, mv1.y, mv1.z, mv1.w};
-    return mu_from_f32(__uint_as_float(w[j]));
+    return MU == SKV_MU_BF16 ? mu_from_bf16(ms[j]) : mu_from_f32(__uint_as_float(ms[j]));
   }
 };
 
@@ -218,33 +215,51 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
   const Geo &g = a.g;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int D = (int)g.D;
+  constexpr int kStep = kLanes * kBatch;  // scalars of one batch of the wave
   for (int64_t chunk = (int64_t)blockIdx.x * kEncWaves + wave; chunk < g.n_chunks;
        chunk += (int64_t)gridDim.x * kEncWaves) {
     const int64_t row = chunk / g.ntb, blk = chunk - row * g.ntb;
     const int64_t tok = min<int64_t>(kChunkTokens, g.tokens - blk * kChunkTokens);
-    const int ngroups = (int)(tok * g.D / kGroup);
+    const int nsc = (int)(tok * D);
     const int64_t base = (row * g.tokens + blk * kChunkTokens) * g.D;
 
-    // the lane's 8 channels are fixed because 512 is a multiple of head_dim
-    const int d0 = (kGroup * lane) % (int)g.D;
-    float s[kGroup];
+    // symbol k of the lane has channel (lane + 64 k) mod D; with D a power of
+    // two up to 512 that repeats with a period dividing kBatch
+    float s[kBatch];
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) s[j] = a.scale[row * g.D + d0 + j];
+    for (int j = 0; j < kBatch; ++j) s[j] = a.scale[row * g.D + ((lane + kLanes * j) & (D - 1))].x;
 
     LaneCoder cod;
-    cod.init(reinterpret_cast<uint32_t *>(a.scratch + ((uint64_t)chunk * kLanes + lane) * g.lane_cap),
-             g.lane_cap / 4);
+    cod.init(reinterpret_cast<uint32_t *>(a.scratch + (uint64_t)chunk * kLanes * g.lane_cap) + lane, g.lane_cap / 4);
 
-    Group<SYM, MU> cur;
-    if (lane < ngroups) cur.load(a, base + (int64_t)lane * kGroup);
-    for (int grp = lane; grp < ngroups; grp += kLanes) {
-      Group<SYM, MU> nxt;
-      if (grp + kLanes < ngroups) nxt.load(a, base + (int64_t)(grp + kLanes) * kGroup);  // in flight meanwhile
+    const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;  // this lane's symbols
+    const int nfull = nsc / kStep;                                         // batches every lane fills
+    const int nb = (nsc + kStep - 1) / kStep;
+    Batch<SYM, MU> cur, nxt;
+    if (nfull > 0) cur.load_full(a, base + lane);
+    else cur.load_part(a, base + lane, nk);
+    for (int b = 0; b < nb; ++b) {
+      const int64_t i1 = base + lane + (int64_t)(b + 1) * kStep;
+      if (b + 1 < nfull) nxt.load_full(a, i1);  // in flight meanwhile
+      else if (b + 1 < nb) nxt.load_part(a, i1, nk - (b + 1) * kBatch);
+      if (b < nfull) {
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        uint32_t c, f;
-        model_pair<SYM, FAST>(a, t, cur.sym(j), cur.mu(j), s[j], c, f);
-        cod.encode(c, f);
+        for (int j = 0; j < kBatch; ++j) {
+          uint32_t c, f;
+          model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), s[j], c, f);
+          cod.encode(c, f);
+        }
+      } else {
+        const int v = nk - b * kBatch;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (j < v) {
+            uint32_t c, f;
+            model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), s[j], c, f);
+            cod.encode(c, f);
+          }
+        }
       }
       cur = nxt;
     }
@@ -257,7 +272,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     a.lens[chunk * kLanes + lane] = nbytes;
     uint32_t tot = nbytes;
     for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
-    if (lane == 0) a.sizes[chunk] = kHeaderBytes + (uint64_t)tot;
+    if (lane == 0) a.sizes[chunk] = ((uint64_t)kHeaderBytes + tot + 3) & ~3ull;
   }
 }
 
@@ -316,52 +331,52 @@ __global__ __launch_bounds__(1024) void k_offsets(const uint64_t *__restrict__ s
 }
 
 // ---- compaction: one block per chunk ----
-// The chunk occupies bytes [o0, o1) of the stream: the u16 length header, then
-// substream l at [p_l, p_l + len_l), p_l = o0 + 128 + (lengths before l).  A
-// wave copies one substream at a time: the aligned words inside it are funnel
-// shifts of two scratch words (coalesced stores), and the at most 3 + 3 bytes
-// it shares with a neighbour's words are written byte by byte.
+// Chunk c occupies [o0, o1) of the stream, o0 a multiple of 4: the u16 length
+// header; the first m words of every lane, already interleaved in the scratch
+// slot (word w of lane l at word 64 w + l), copied as they are; each lane's
+// remaining len - 4m bytes, lane after lane; zeros up to o1.
 __global__ __launch_bounds__(256) void k_compact(const uint32_t *__restrict__ lens_g, const uint8_t *__restrict__ scratch,
                                                  const uint64_t *__restrict__ offsets, uint8_t *__restrict__ bits,
                                                  uint64_t cap, uint32_t lane_cap) {
-  __shared__ uint32_t pre[kLanes + 1];
+  __shared__ uint32_t s_tail[kLanes + 1];  // exclusive prefix of the lanes' remaining bytes
+  __shared__ uint32_t s_m;
   const int64_t chunk = blockIdx.x;
   const uint64_t o0 = offsets[chunk], o1 = offsets[chunk + 1];
   if (o1 > cap) return;  // capacity error already recorded; write nothing past the buffer
   const int t = threadIdx.x;
+  const uint8_t *src = scratch + (uint64_t)chunk * kLanes * lane_cap;
   if (t < kLanes) {
     const uint32_t len = lens_g[chunk * kLanes + t];
-    bits[o0 + 2 * t] = (uint8_t)(len & 0xFFu);
-    bits[o0 + 2 * t + 1] = (uint8_t)(len >> 8);
-    uint32_t inc = len;
+    reinterpret_cast<uint16_t *>(bits + o0)[t] = (uint16_t)len;
+    uint32_t m = len >> 2;
+    for (int off = 32; off > 0; off >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    uint32_t inc = len - 4 * m;
     for (int off = 1; off < 64; off <<= 1) {
       const uint32_t v = __shfl_up(inc, off, 64);
       if (t >= off) inc += v;
     }
-    pre[t + 1] = inc;
-    if (t == 0) pre[0] = 0;
+    s_tail[t + 1] = inc;
+    if (t == 0) {
+      s_tail[0] = 0;
+      s_m = m;
+    }
   }
   __syncthreads();
-  const int lane = t & 63, wave = t >> 6;
-  for (int l = wave; l < kLanes; l += 4) {
-    const uint64_t a = o0 + kHeaderBytes + pre[l];
-    const uint64_t b = o0 + kHeaderBytes + pre[l + 1];
-    const uint8_t *src = scratch + ((uint64_t)chunk * kLanes + l) * lane_cap;
-    const uint64_t wa = (a + 3) & ~3ull, wb = b & ~3ull;  // aligned words fully inside [a, b)
-    if (wa < wb) {
-      const uint32_t sh = 8 * (uint32_t)((wa - a) & 3);
-      const uint32_t *sw0 = reinterpret_cast<const uint32_t *>(src) + ((wa - a) >> 2);
-      for (uint64_t q = wa + 4 * (uint64_t)lane; q < wb; q += 256) {
-        const uint32_t *sw = sw0 + ((q - wa) >> 2);
-        const uint32_t w0 = __builtin_bswap32(sw[0]);
-        const uint32_t v = sh ? (w0 << sh) | (__builtin_bswap32(sw[1]) >> (32 - sh)) : w0;
-        *reinterpret_cast<uint32_t *>(bits + q) = __builtin_bswap32(v);
-      }
-      if (lane < 3 && a + lane < wa) bits[a + lane] = src[lane];                       // head
-      if (lane < 3 && wb + lane < b) bits[wb + lane] = src[wb + lane - a];             // tail
-    } else if (lane < 8 && a + lane < b) {
-      bits[a + lane] = src[lane];  // short substream: no whole word inside
-    }
+  const uint32_t m = s_m;
+  const uint32_t *sw = reinterpret_cast<const uint32_t *>(src);
+  uint32_t *dw = reinterpret_cast<uint32_t *>(bits + o0 + kHeaderBytes);
+  for (uint32_t q = t; q < kLanes * m; q += 256) dw[q] = sw[q];
+  // the rest of lane l: 4 threads per lane, byte j of the tail is byte 4m + j of the lane
+  const int l = t & 63;
+  const uint64_t d0 = o0 + kHeaderBytes + 4ull * kLanes * m + s_tail[l];
+  const uint32_t n = s_tail[l + 1] - s_tail[l];
+  for (uint32_t j = (uint32_t)(t >> 6); j < n; j += 4) {
+    const uint32_t wi = m + (j >> 2);
+    bits[d0 + j] = src[4u * (wi * kLanes + (uint32_t)l) + (j & 3u)];
+  }
+  if (t < 3) {
+    const uint64_t end = o0 + kHeaderBytes + 4ull * kLanes * m + s_tail[kLanes];
+    if (end + t < o1) bits[end + t] = 0;
   }
 }
 

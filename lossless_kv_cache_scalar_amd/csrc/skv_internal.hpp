@@ -18,7 +18,7 @@ namespace skv {
 
 constexpr int kChunkTokens = 256;
 constexpr int kLanes = 64;        // one wavefront: one lane per substream
-constexpr int kGroup = 8;         // consecutive scalars a lane takes at a time
+constexpr int kBatch = 8;         // symbols a lane loads ahead at a time
 constexpr int kKnotsPerUnit = 64; // knot spacing 1/64 in z
 constexpr int kUMax = 1024;       // knots cover |z| <= 16
 constexpr int kNKnot = 2 * kUMax + 1;
@@ -63,7 +63,7 @@ struct Workspace {
   int32_t *aflag;     // 1 when every window's offsets fit 16 bits
   float2 *uinv;       // kNInv + 1: (u, du) at y = m * MG / kNInv
   float2 *etab;       // 256 e4m3 bins (lo, hi), indexed by pattern
-  float *scale;       // per channel: RN32(64 / max(sigma, 2^-100))
+  float2 *scale;      // per channel: (s, ~1/s), s = RN32(64 / max(sigma, 2^-100))
   uint32_t *lens;     // n_chunks * 64 substream lengths (encode)
   uint64_t *sizes;    // n_chunks chunk sizes (encode)
   uint8_t *scratch;   // n_chunks * 64 * lane_cap (encode)

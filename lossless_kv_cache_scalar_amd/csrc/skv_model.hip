@@ -174,8 +174,9 @@ __global__ void k_etab(float2 *__restrict__ etab) {
 // ---------------------------------------------------------------- scales
 // s_c = RN32(64 / max(sigma_c, 2^-100)): the fp64 quotient of two fp32 values
 // rounds to the same fp32 as the exact quotient (53 >= 2 * 24 + 2).
-// sigma must be finite and >= 0.
-__global__ void k_scale(const float *__restrict__ sigma, float *__restrict__ scale, int64_t n, int32_t *status) {
+// sigma must be finite and >= 0.  The second member, an approximate 1 / s,
+// only steers the decoder's first guesses.
+__global__ void k_scale(const float *__restrict__ sigma, float2 *__restrict__ scale, int64_t n, int32_t *status) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float sg = sigma[i];
@@ -184,7 +185,8 @@ __global__ void k_scale(const float *__restrict__ sigma, float *__restrict__ sca
     sg = 1.0f;
   }
   float sp = sg > 0x1p-100f ? sg : 0x1p-100f;
-  scale[i] = (float)(64.0 / (double)sp);
+  const float sc = (float)(64.0 / (double)sp);
+  scale[i] = make_float2(sc, __builtin_amdgcn_rcpf(sc));
 }
 
 __global__ void k_clear_status(int32_t *status) {

@@ -56,7 +56,6 @@ typedef struct {
 /* ---- model geometry ---- */
 #define CHUNK_TOKENS 256
 #define LANES 64
-#define GROUP 8                 /* consecutive scalars a lane takes at a time */
 #define KNOTS_PER_UNIT 64       /* knot spacing 1/64 in z */
 #define U_MAX 1024              /* table covers |z| <= 16 */
 #define N_KNOT (2 * U_MAX + 1)
@@ -416,11 +415,16 @@ static void rc_dec_init(rc_dec *q, const uint8_t *in, size_t len) {
 /*   x and mu are [layers][2 (K, V)][kv_heads][tokens][head_dim].           */
 /*   A chunk is one (layer, kv, head) row's block of 256 tokens (the last   */
 /*   block may be shorter); chunk id = row * ceil(tokens/256) + block.      */
-/*   Inside a chunk the scalars are in memory order, i = t * D + d.  They   */
-/*   are cut into groups of 8; group g goes to lane g mod 64, and a lane    */
-/*   codes its groups in increasing g, each group's 8 scalars in order.     */
-/*   Each lane is one range-coded substream.                                */
-/*   Chunk bytes: u16 len[64] (little-endian), then the 64 substreams.      */
+/*   Inside a chunk the scalars are in memory order, i = t * D + d.         */
+/*   Scalar i goes to lane i mod 64, and a lane codes its scalars in        */
+/*   increasing i.  Each lane is one range-coded substream of len[l] >= 1   */
+/*   bytes.                                                                 */
+/*   Chunk bytes:                                                           */
+/*     u16 len[64], little-endian;                                          */
+/*     the interleaved words: with m = min over lanes of floor(len[l] / 4), */
+/*       for w = 0 .. m-1, for l = 0 .. 63: bytes 4w .. 4w+3 of lane l;    */
+/*     the tails: for l = 0 .. 63, bytes 4m .. len[l]-1 of lane l;          */
+/*     zero bytes up to a multiple of 4.                                    */
 /*   offsets[0] = 0, chunk c occupies [offsets[c], offsets[c+1]).           */
 /* ------------------------------------------------------------------------ */
 static int shape_ok(const ref_shape *sh) {
@@ -428,7 +432,8 @@ static int shape_ok(const ref_shape *sh) {
   if (sh->layers < 1 || sh->kv_heads < 1 || sh->tokens < 1 || sh->head_dim < 1) return REF_ERR_ARG;
   if (sh->sym_fmt != REF_SYM_BF16 && sh->sym_fmt != REF_SYM_E4M3) return REF_ERR_ARG;
   if (sh->mu_fmt != REF_MU_BF16 && sh->mu_fmt != REF_MU_F32) return REF_ERR_ARG;
-  if (sh->head_dim % GROUP != 0 || (GROUP * LANES) % sh->head_dim != 0) return REF_ERR_UNSUPPORTED;
+  /* head_dim a power of two from 8 to 512 (a multiple of 8 dividing 512) */
+  if (sh->head_dim % 8 != 0 || 512 % sh->head_dim != 0) return REF_ERR_UNSUPPORTED;
   return REF_OK;
 }
 
@@ -438,12 +443,13 @@ int64_t skvref_num_chunks(const ref_shape *sh) {
   return sh->layers * 2 * sh->kv_heads * ntb;
 }
 
-/* worst case: 3 bytes per symbol (a frequency of 1 in 2^24), 1 flush byte per lane */
+/* worst case: 3 bytes per symbol (a frequency of 1 in 2^24), 1 flush byte per
+   lane, 3 bytes of padding per chunk */
 uint64_t skvref_encode_bound(const ref_shape *sh) {
   int64_t nc = skvref_num_chunks(sh);
   if (nc < 0) return 0;
   uint64_t nsc = (uint64_t)sh->layers * 2 * sh->kv_heads * sh->tokens * sh->head_dim;
-  return (uint64_t)nc * (HEADER_BYTES + LANES) + 3 * nsc;
+  return (uint64_t)nc * (HEADER_BYTES + LANES + 3) + 3 * nsc;
 }
 
 static uint32_t sym_at(int fmt, const void *x, int64_t i) {
@@ -457,7 +463,7 @@ static float mu_at(int fmt, const void *mu, int64_t i) {
 }
 
 typedef struct {
-  int64_t row, block, tok, nsc, ngroups;
+  int64_t row, block, tok, nsc;
   int64_t base;  /* index of the chunk's first scalar in x / mu */
 } chunk_geo;
 
@@ -469,9 +475,24 @@ static chunk_geo geometry(const ref_shape *sh, int64_t chunk) {
   g.tok = sh->tokens - g.block * CHUNK_TOKENS;
   if (g.tok > CHUNK_TOKENS) g.tok = CHUNK_TOKENS;
   g.nsc = g.tok * sh->head_dim;
-  g.ngroups = g.nsc / GROUP;
   g.base = g.row * sh->tokens * sh->head_dim + g.block * CHUNK_TOKENS * sh->head_dim;
   return g;
+}
+
+/* m: the number of whole 4-byte words every lane has */
+static uint64_t common_words(const uint64_t *lens) {
+  uint64_t m = lens[0] / 4;
+  for (int l = 1; l < LANES; l++)
+    if (lens[l] / 4 < m) m = lens[l] / 4;
+  return m;
+}
+
+/* chunk byte position of byte j of lane l's substream */
+static uint64_t lane_byte_pos(const uint64_t *lens, uint64_t m, int l, uint64_t j) {
+  if (j < 4 * m) return HEADER_BYTES + 4 * ((j / 4) * LANES + (uint64_t)l) + (j % 4);
+  uint64_t p = HEADER_BYTES + 4 * m * LANES;
+  for (int k = 0; k < l; k++) p += lens[k] - 4 * m;
+  return p + (j - 4 * m);
 }
 
 /*
@@ -488,34 +509,41 @@ uint64_t skvref_encode_chunk(const ref_model *m, const ref_shape *sh, int64_t ch
   uint32_t up = 24u - m->log2T;  /* scale to the coder's 2^24 total */
   float s[512];
   for (int64_t d = 0; d < D; d++) s[d] = skvref_scale(sigma_row[d]);
-  uint8_t *lane_buf = (uint8_t *)malloc((size_t)(3 * 4 * D + 8));
-  uint64_t pos = HEADER_BYTES;
-  *status = REF_OK;
+  size_t lane_cap = (size_t)(3 * 4 * D + 8);
+  uint8_t *lane_buf = (uint8_t *)malloc(lane_cap * LANES);
+  uint64_t lens[LANES];
   for (int lane = 0; lane < LANES; lane++) {
     rc_enc e;
-    rc_enc_init(&e, lane_buf, (size_t)(3 * 4 * D + 8));
-    for (int64_t grp = lane; grp < g.ngroups; grp += LANES) {
-      for (int j = 0; j < GROUP; j++) {
-        int64_t i = grp * GROUP + j;
-        uint32_t b = sym_at(sh->sym_fmt, x_c, i);
-        float mu = mu_at(sh->mu_fmt, mu_c, i);
-        uint32_t clo, chi;
-        skvref_cum_pair(m, mu, s[i % D], b, &clo, &chi);
-        rc_encode(&e, (uint64_t)clo << up, (uint64_t)(chi - clo) << up);
-      }
+    rc_enc_init(&e, lane_buf + lane_cap * lane, lane_cap);
+    for (int64_t i = lane; i < g.nsc; i += LANES) {
+      uint32_t b = sym_at(sh->sym_fmt, x_c, i);
+      float mu = mu_at(sh->mu_fmt, mu_c, i);
+      uint32_t clo, chi;
+      skvref_cum_pair(m, mu, s[i % D], b, &clo, &chi);
+      rc_encode(&e, (uint64_t)clo << up, (uint64_t)(chi - clo) << up);
     }
     rc_finish(&e);
-    if (cap >= 2u * (uint64_t)(lane + 1)) {
-      out[2 * lane] = (uint8_t)(e.n & 0xFF);
-      out[2 * lane + 1] = (uint8_t)(e.n >> 8);
+    lens[lane] = e.n;
+  }
+  uint64_t total = HEADER_BYTES;
+  for (int l = 0; l < LANES; l++) total += lens[l];
+  uint64_t size = (total + 3) & ~3ull;
+  uint64_t mw = common_words(lens);
+  *status = REF_OK;
+  for (uint64_t p = 0; p < size && p < cap; p++) out[p] = 0;
+  for (int l = 0; l < LANES; l++) {
+    if (2u * (uint64_t)l + 1 < cap) {
+      out[2 * l] = (uint8_t)(lens[l] & 0xFF);
+      out[2 * l + 1] = (uint8_t)(lens[l] >> 8);
     }
-    for (size_t t = 0; t < e.n; t++)
-      if (pos + t < cap) out[pos + t] = lane_buf[t];
-    pos += e.n;
+    for (uint64_t j = 0; j < lens[l]; j++) {
+      uint64_t p = lane_byte_pos(lens, mw, l, j);
+      if (p < cap) out[p] = lane_buf[lane_cap * l + j];
+    }
   }
   free(lane_buf);
-  if (pos > cap) *status = REF_ERR_CAPACITY;
-  return pos;
+  if (size > cap) *status = REF_ERR_CAPACITY;
+  return size;
 }
 
 /*
@@ -542,51 +570,45 @@ int skvref_decode_chunk(const ref_model *m, const ref_shape *sh, int64_t chunk,
     total += lens[l];
     if (lens[l] == 0) st = REF_ERR_CORRUPT;
   }
-  if (total != nbytes) {
+  if (((total + 3) & ~3ull) != nbytes) {
     st = REF_ERR_CORRUPT;
-    /* keep every substream inside the chunk */
-    uint64_t p = HEADER_BYTES;
-    for (int l = 0; l < LANES; l++) {
-      if (p + lens[l] > nbytes) lens[l] = p < nbytes ? nbytes - p : 0;
-      p += lens[l];
-    }
+    for (int l = 0; l < LANES; l++) lens[l] = 0;  /* read nothing */
   }
-  uint64_t start = HEADER_BYTES;
-  for (int lane = 0; lane < LANES; lane++) {
+  uint64_t mw = common_words(lens);
+  uint8_t *lane = (uint8_t *)malloc((size_t)nbytes + 1);
+  for (int l = 0; l < LANES; l++) {
+    for (uint64_t j = 0; j < lens[l]; j++) lane[j] = bytes[lane_byte_pos(lens, mw, l, j)];
     rc_dec q;
-    rc_dec_init(&q, bytes + start, (size_t)lens[lane]);
+    rc_dec_init(&q, lane, (size_t)lens[l]);
     uint64_t shifts = 0;
-    for (int64_t grp = lane; grp < g.ngroups; grp += LANES) {
-      for (int j = 0; j < GROUP; j++) {
-        int64_t i = grp * GROUP + j;
-        float mp = mu_prime(mu_at(sh->mu_fmt, mu_c, i));
-        float sc = s[i % D];
-        uint64_t r = q.range >> 24;
-        uint64_t t = q.d / (r << up);
-        if (t >= m->T) { st = REF_ERR_CORRUPT; t = m->T - 1; }
-        /* the unique k with cum(k) <= t < cum(k+1), by bisection over ranks */
-        uint32_t lo = 0, hi = m->N;
-        while (hi - lo > 1) {
-          uint32_t mid = (lo + hi) / 2;
-          if (cum_rank(m, mp, sc, mid) <= t) lo = mid; else hi = mid;
-        }
-        uint32_t c = cum_rank(m, mp, sc, lo);
-        uint32_t f = cum_rank(m, mp, sc, lo + 1) - c;
-        q.d -= r * ((uint64_t)c << up);
-        q.range = r * ((uint64_t)f << up);
-        while (q.range < TOP40) {
-          q.d = ((q.d << 8) | rc_byte(&q)) & W48;
-          q.range <<= 8;
-          shifts++;
-        }
-        uint32_t b = skvref_unrank(m->fmt, lo);
-        if (sh->sym_fmt == REF_SYM_BF16) ((uint16_t *)x_out_c)[i] = (uint16_t)b;
-        else ((uint8_t *)x_out_c)[i] = (uint8_t)b;
+    for (int64_t i = l; i < g.nsc; i += LANES) {
+      float mp = mu_prime(mu_at(sh->mu_fmt, mu_c, i));
+      float sc = s[i % D];
+      uint64_t r = q.range >> 24;
+      uint64_t t = q.d / (r << up);
+      if (t >= m->T) { st = REF_ERR_CORRUPT; t = m->T - 1; }
+      /* the unique k with cum(k) <= t < cum(k+1), by bisection over ranks */
+      uint32_t lo = 0, hi = m->N;
+      while (hi - lo > 1) {
+        uint32_t mid = (lo + hi) / 2;
+        if (cum_rank(m, mp, sc, mid) <= t) lo = mid; else hi = mid;
       }
+      uint32_t c = cum_rank(m, mp, sc, lo);
+      uint32_t f = cum_rank(m, mp, sc, lo + 1) - c;
+      q.d -= r * ((uint64_t)c << up);
+      q.range = r * ((uint64_t)f << up);
+      while (q.range < TOP40) {
+        q.d = ((q.d << 8) | rc_byte(&q)) & W48;
+        q.range <<= 8;
+        shifts++;
+      }
+      uint32_t b = skvref_unrank(m->fmt, lo);
+      if (sh->sym_fmt == REF_SYM_BF16) ((uint16_t *)x_out_c)[i] = (uint16_t)b;
+      else ((uint8_t *)x_out_c)[i] = (uint8_t)b;
     }
-    if (lens[lane] == 0 || shifts + 1 != lens[lane]) st = REF_ERR_CORRUPT;
-    start += lens[lane];
+    if (lens[l] == 0 || shifts + 1 != lens[l]) st = REF_ERR_CORRUPT;
   }
+  free(lane);
   return st;
 }
 
@@ -655,7 +677,7 @@ int skvref_encode_m(const ref_model *m, const ref_shape *sh, const void *x, cons
   work *ws = (work *)calloc((size_t)nthreads, sizeof(work));
   pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
   uint64_t *sizes = (uint64_t *)calloc((size_t)nc, sizeof(uint64_t));
-  uint64_t per_chunk_max = HEADER_BYTES + LANES + 3ull * CHUNK_TOKENS * (uint64_t)sh->head_dim;
+  uint64_t per_chunk_max = HEADER_BYTES + LANES + 3 + 3ull * CHUNK_TOKENS * (uint64_t)sh->head_dim;
   int st = REF_OK;
   for (int t = 0; t < nthreads; t++) {
     work *w = &ws[t];

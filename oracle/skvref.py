@@ -173,7 +173,7 @@ class Model:
     def encode_chunk(self, shape: Shape, chunk: int, x_c, mu_c, sigma_row):
         """Encode one chunk from its own slices (x_c, mu_c start at the chunk)."""
         L = lib()
-        cap = 128 + 64 + 3 * 256 * shape.head_dim
+        cap = 128 + 64 + 3 + 3 * 256 * shape.head_dim
         out = np.zeros(cap, dtype=np.uint8)
         st = C.c_int(0)
         n = L.skvref_encode_chunk(self.ptr, C.byref(shape), chunk, _p(x_c), _p(mu_c), _p(sigma_row),

@@ -144,7 +144,7 @@ def test_roundtrip_ragged_chunks(tokens, head_dim):
     # every lane has at least its flush byte, even with no symbols
     for c in range(len(offs) - 1):
         lens = np.frombuffer(bits[int(offs[c]):int(offs[c]) + 128].tobytes(), dtype="<u2")
-        assert lens.min() >= 1 and int(offs[c + 1] - offs[c]) == 128 + int(lens.sum())
+        assert lens.min() >= 1 and int(offs[c + 1] - offs[c]) == (128 + int(lens.sum()) + 3) // 4 * 4
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
@@ -160,8 +160,7 @@ def test_pure_noise_stream_lengths(fmt):
     for c in range(len(offs) - 1):
         lens = np.frombuffer(bits[int(offs[c]):int(offs[c]) + 128].tobytes(), dtype="<u2").astype(int)
         tok = min(256, w.tokens - 256 * (c % 2))
-        groups = tok * w.head_dim // 8
-        n_lane = np.array([8 * len(range(l, groups, 64)) for l in range(64)])
+        n_lane = np.array([len(range(l, tok * w.head_dim, 64)) for l in range(64)])
         np.testing.assert_array_equal(lens, (2 if fmt == 0 else 1) * n_lane + 1)
     out, st = m.decode(sh, bits, offs, mu, np.ones(w.n_channels, np.float32))
     assert st == R.OK and np.array_equal(out, x)
@@ -292,3 +291,53 @@ def test_chunk_api_matches_whole_cache():
         st = m.decode_chunk(sh, c, got, mf[base:], sigma[row * w.head_dim:], out)
         n = min(256, w.tokens - 256 * blk) * w.head_dim
         assert st == R.OK and np.array_equal(out[:n], xf[base:base + n])
+
+
+def _lane_bytes_from_chunk(chunk):
+    """The 64 substreams of a chunk, read back by the layout rule: a header of
+    u16 lengths, then m words of every lane interleaved word by word (m = the
+    fewest whole words any lane has), then each lane's remaining bytes in lane
+    order, then zero padding to a multiple of 4."""
+    lens = [int(chunk[2 * l]) | int(chunk[2 * l + 1]) << 8 for l in range(64)]
+    m = min(n // 4 for n in lens)
+    lanes = [bytearray() for _ in range(64)]
+    p = 128
+    for w in range(m):
+        for l in range(64):
+            lanes[l] += bytes(chunk[p:p + 4])
+            p += 4
+    for l in range(64):
+        lanes[l] += bytes(chunk[p:p + lens[l] - 4 * m])
+        p += lens[l] - 4 * m
+    assert len(chunk) == (p + 3) // 4 * 4 and not np.any(chunk[p:])
+    return lanes
+
+
+@pytest.mark.parametrize("tokens,head_dim,fmt", [(256, 128, 0), (300, 64, 0), (3, 8, 0), (200, 128, 1), (1, 512, 1)])
+def test_chunk_layout_is_the_lane_substreams(tokens, head_dim, fmt):
+    """Every chunk is its 64 substreams laid out by the layout rule, and
+    substream l is the range code (pinned above by the unbounded-integer
+    statement) of the chunk's scalars l, l + 64, l + 128, ... in that order."""
+    w = synth.Workload("t", 1, 1, 2, head_dim, tokens, fmt, 1 if fmt else 0, 0.02, 1, 64)
+    x, mu = _cache(w)
+    rng = np.random.default_rng(tokens + head_dim)
+    sigma = (0.02 * np.exp(rng.standard_normal(w.n_channels))).astype(np.float32)
+    m = R.Model(fmt, rng.integers(0, 50, 65536 if fmt == 0 else 256).astype(np.uint64))
+    sh = _shape(w)
+    bits, offs = m.encode(sh, x, mu, sigma)
+    xs = x.reshape(-1, tokens * head_dim)
+    mus = mu.reshape(-1, tokens * head_dim)
+    if w.mu_fmt == 0:
+        mus = (mus.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    ntb = (tokens + 255) // 256
+    up = 0 if fmt == 0 else 8
+    for c in range(len(offs) - 1):
+        row, blk = divmod(c, ntb)
+        lo_i, hi_i = blk * 256 * head_dim, min(tokens, (blk + 1) * 256) * head_dim
+        lanes = _lane_bytes_from_chunk(bits[int(offs[c]):int(offs[c + 1])])
+        sc = R.scale(sigma[row * head_dim:(row + 1) * head_dim])
+        for l in range(64):
+            idx = np.arange(lo_i + l, hi_i, 64)
+            clo, chi = m.cum_pair(mus[row, idx], sc[idx % head_dim], xs[row, idx].astype(np.uint32))
+            want = R.rc_encode_seq(clo.astype(np.uint64) << up, (chi - clo).astype(np.uint64) << up)
+            assert bytes(lanes[l]) == bytes(want), (c, l)
