@@ -46,48 +46,54 @@ struct DecArgs {
 };
 
 // Bits of one lane's substream, most significant first; bytes at or past its
-// length read as 0.  ib holds the bits before word w; the two aligned dwords
-// that hold word w are in flight in (plo, phi) from the moment word w - 1 is
-// taken until take() needs word w.
+// length read as 0.  ib holds the bits before word w.  After every symbol,
+// issue() loads the dword(s) that hold word w into (plo, phi), so take() in
+// the next symbol finds them one symbol old: every symbol issues the same
+// memory operations, and the waits stay short.  Words w < m are aligned
+// dwords of the interleaved region (no masking); the lane's tail words may
+// straddle dwords and run past its length.
 struct LaneReader {
   const uint8_t *chunk;  // chunk start, 4-byte aligned
   uint32_t csize;        // chunk bytes (a multiple of 4, >= 192)
   uint32_t m;            // interleaved words per lane
-  uint32_t lane, tail, len;
+  uint32_t tail, len;    // chunk offset of the lane's tail, lane length
+  uint32_t ip;           // chunk offset of interleaved word w of the lane
   uint32_t w, plo, phi;
   uint64_t ib;  // next bits, left-aligned
   int nib;      // valid bits in ib
 
-  // chunk byte offset of byte 4 wi of the lane
-  __device__ __forceinline__ uint32_t pos(uint32_t wi) const {
-    return wi < m ? kHeaderBytes + 4u * (wi * kLanes + lane) : tail + 4u * (wi - m);
-  }
   __device__ __forceinline__ void issue() {
-    const uint32_t p = pos(w);
-    uint32_t a0 = p & ~3u;
+    const bool tl = w >= m;
+    uint32_t a0 = tl ? (tail + 4u * (w - m)) & ~3u : ip;
     if (4u * w >= len) a0 = 0u;  // nothing left: any dword of the chunk, masked off below
-    uint32_t a1 = a0 + 4u;
-    if (a1 >= csize) a1 = a0;
     plo = *reinterpret_cast<const uint32_t *>(chunk + a0);
-    phi = *reinterpret_cast<const uint32_t *>(chunk + a1);
+    if (__builtin_expect(__any(tl), 0)) {
+      uint32_t a1 = a0 + 4u;
+      if (a1 >= csize) a1 = a0;
+      phi = *reinterpret_cast<const uint32_t *>(chunk + a1);
+    }
   }
   __device__ __forceinline__ uint32_t word() const {
-    const uint32_t sh = 8u * (pos(w) & 3u);
+    if (__builtin_expect(w < m, 1)) return __builtin_bswap32(plo);
+    const uint32_t sh = 8u * (tail & 3u);
     uint32_t v = __builtin_bswap32((uint32_t)((((uint64_t)phi << 32) | plo) >> sh));
     const int valid = (int)len - 4 * (int)w;
     if (valid <= 0) return 0u;
     if (valid < 4) v &= ~(0xFFFFFFFFu >> (8 * valid));
     return v;
   }
-  __device__ __forceinline__ void init() {
+  __device__ __forceinline__ void init(uint32_t lane) {
     w = 0;
+    ip = kHeaderBytes + 4u * lane;
     issue();
     ib = (uint64_t)word() << 32;
     w = 1;
+    ip += 4u * kLanes;
     issue();
     ib |= word();
     nib = 64;
     w = 2;
+    ip += 4u * kLanes;
     issue();
   }
   // n in {0, 8, 16, 24}
@@ -96,7 +102,7 @@ struct LaneReader {
       ib |= (uint64_t)word() << (32 - nib);
       nib += 32;
       ++w;
-      issue();
+      ip += 4u * kLanes;
     }
     const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)(ib >> 32), (0u - n) & 31u, n);
     ib <<= n;
@@ -211,10 +217,6 @@ struct MuBatch {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) v[j] = one(mu, i0 + kLanes * j);
   }
-  __device__ __forceinline__ void load_part(const void *mu, uint32_t i0, int valid) {
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) v[j] = j < valid ? one(mu, i0 + kLanes * j) : 0u;
-  }
   __device__ __forceinline__ float get(int j) const {
     return MU == SKV_MU_BF16 ? mu_from_bf16(v[j]) : mu_from_f32(__uint_as_float(v[j]));
   }
@@ -317,10 +319,9 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     br.chunk = a.bits + o0;
     br.csize = (uint32_t)nbytes;
     br.m = mw;
-    br.lane = (uint32_t)lane;
     br.tail = kHeaderBytes + 4u * kLanes * mw + inc - (len - 4u * mw);
     br.len = len;
-    br.init();
+    br.init((uint32_t)lane);
     uint64_t d = (uint64_t)br.take(24) << 24;
     d |= br.take(24);
     uint64_t range = kW48;
@@ -340,35 +341,46 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     void *x_ch = BF ? (void *)(static_cast<uint16_t *>(a.x_out) + base) : (void *)(static_cast<uint8_t *>(a.x_out) + base);
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;
     const int nfull = nsc / kStep;
-    const int nb = (nsc + kStep - 1) / kStep;
     MuBatch<MU> cur, nxt;
     if (nfull > 0) cur.load_full(mu_ch, lane);
-    else cur.load_part(mu_ch, lane, nk);
-    for (int b = 0; b < nb; ++b) {
+    for (int b = 0; b < nfull; ++b) {
       const uint32_t i0 = (uint32_t)lane + (uint32_t)b * kStep;
+      // this batch's means, loaded one batch ago, as floats now: the wait for
+      // them happens here and not inside the symbols
+      float mf[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        mf[j] = cur.get(j);
+        asm volatile("" : "+v"(mf[j]));
+      }
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
-      else if (b + 1 < nb) nxt.load_part(mu_ch, i0 + kStep, nk - (b + 1) * kBatch);
-      if (b < nfull) {
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, cur.get(j), s[j],
-                                                          sinv[j]);
-          if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
-          else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
-        }
-      } else {
-        const int v = nk - b * kBatch;
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          if (j < v) {
-            const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, cur.get(j),
-                                                            s[j], sinv[j]);
-            if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
-            else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
-          }
-        }
+      for (int j = 0; j < kBatch; ++j) {
+        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, mf[j], s[j], sinv[j]);
+        br.issue();
+        if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
+        else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
       }
       cur = nxt;
+    }
+    // the last, partial batch of a short chunk: symbol by symbol
+    for (int k = nfull * kBatch; k < nk; ++k) {
+      const uint32_t i = (uint32_t)lane + (uint32_t)k * kLanes;
+      const int j = k & (kBatch - 1);
+      float sj = s[0], sij = sinv[0];
+#pragma unroll
+      for (int q = 1; q < kBatch; ++q) {
+        if (j == q) {
+          sj = s[q];
+          sij = sinv[q];
+        }
+      }
+      const uint32_t mraw = cur.one(mu_ch, i);
+      const float m = MU == SKV_MU_BF16 ? mu_from_bf16(mraw) : mu_from_f32(__uint_as_float(mraw));
+      const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, m, sj, sij);
+      br.issue();
+      if (BF) static_cast<uint16_t *>(x_ch)[i] = (uint16_t)gs;
+      else static_cast<uint8_t *>(x_ch)[i] = (uint8_t)gs;
     }
     // a substream of n renormalisations holds n + 1 bytes
     if (shifted + 1 != len) corrupt = true;
