@@ -336,27 +336,32 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       s[j] = sc.x;
       sinv[j] = sc.y;
     }
+    // wait for the scales here: a wait inside the symbol loop would also wait
+    // for the loads in flight on every trip
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(s[j]), "v"(sinv[j]));
     const void *mu_ch = MU == SKV_MU_BF16 ? (const void *)(static_cast<const uint16_t *>(a.mu) + base)
                                           : (const void *)(static_cast<const float *>(a.mu) + base);
     void *x_ch = BF ? (void *)(static_cast<uint16_t *>(a.x_out) + base) : (void *)(static_cast<uint8_t *>(a.x_out) + base);
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;
     const int nfull = nsc / kStep;
     MuBatch<MU> cur, nxt;
-    if (nfull > 0) cur.load_full(mu_ch, lane);
+    if (nfull > 0) {
+      cur.load_full(mu_ch, lane);
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.v[j]));
+    }
     for (int b = 0; b < nfull; ++b) {
       const uint32_t i0 = (uint32_t)lane + (uint32_t)b * kStep;
-      // this batch's means, loaded one batch ago, as floats now: the wait for
-      // them happens here and not inside the symbols
-      float mf[kBatch];
+      // this batch's means were loaded one batch ago; wait for them here, once
+      // per batch, and not inside the symbols
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        mf[j] = cur.get(j);
-        asm volatile("" : "+v"(mf[j]));
-      }
+      for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.v[j]));
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, mf[j], s[j], sinv[j]);
+        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, cur.get(j), s[j],
+                                                        sinv[j]);
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
         else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;

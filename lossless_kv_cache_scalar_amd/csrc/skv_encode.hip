@@ -82,11 +82,15 @@ struct LaneCoder {
     out = o;
   }
 
-  // a valid model never fills the slot; a broken one rewrites its last word
+  // Stores the word that starts at bit nbits - 32 of acc on every symbol, so
+  // every symbol issues the same memory operation (the waits for the batch
+  // loads stay exact); the store is final once those 32 bits are complete and
+  // is rewritten until then.  A valid model never fills the slot; a broken one
+  // rewrites its last word.
   __device__ __forceinline__ void flush_word() {
+    const uint32_t word = (uint32_t)(acc >> ((nbits - 32) & 63));
+    out[min(nw, capw - 1) * kLanes] = __builtin_bswap32(word);
     if (nbits >= 32) {
-      const uint32_t word = (uint32_t)(acc >> (nbits - 32));
-      out[min(nw, capw - 1) * kLanes] = __builtin_bswap32(word);
       ++nw;
       nbits -= 32;
     }
@@ -142,15 +146,6 @@ struct Batch {
   __device__ __forceinline__ void load_full(const EncArgs &a, int64_t i0) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) one(a, i0 + (int64_t)kLanes * j, j);
-  }
-  // only the first `valid` symbols exist (valid may be <= 0)
-  __device__ __forceinline__ void load_part(const EncArgs &a, int64_t i0, int valid) {
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      xs[j] = 0;
-      ms[j] = 0;
-      if (j < valid) one(a, i0 + (int64_t)kLanes * j, j);
-    }
   }
   __device__ __forceinline__ float mu(int j) const {
     return MU == SKV_MU_BF16 ? mu_from_bf16(ms[j]) : mu_from_f32(__uint_as_float(ms[j]));
@@ -229,39 +224,48 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     float s[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) s[j] = a.scale[row * g.D + ((lane + kLanes * j) & (D - 1))].x;
+    // wait for the scales here: a wait inside the symbol loop would also wait
+    // for the batch loads in flight on every trip
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(s[j]));
 
     LaneCoder cod;
     cod.init(reinterpret_cast<uint32_t *>(a.scratch + (uint64_t)chunk * kLanes * g.lane_cap) + lane, g.lane_cap / 4);
 
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;  // this lane's symbols
     const int nfull = nsc / kStep;                                         // batches every lane fills
-    const int nb = (nsc + kStep - 1) / kStep;
     Batch<SYM, MU> cur, nxt;
-    if (nfull > 0) cur.load_full(a, base + lane);
-    else cur.load_part(a, base + lane, nk);
-    for (int b = 0; b < nb; ++b) {
-      const int64_t i1 = base + lane + (int64_t)(b + 1) * kStep;
-      if (b + 1 < nfull) nxt.load_full(a, i1);  // in flight meanwhile
-      else if (b + 1 < nb) nxt.load_part(a, i1, nk - (b + 1) * kBatch);
-      if (b < nfull) {
+    if (nfull > 0) {
+      cur.load_full(a, base + lane);
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          uint32_t c, f;
-          model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), s[j], c, f);
-          cod.encode(c, f);
-        }
-      } else {
-        const int v = nk - b * kBatch;
+      for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
+    }
+    for (int b = 0; b < nfull; ++b) {
+      // this batch's symbols and means were loaded one batch ago; wait for
+      // them here, once per batch, and not inside the symbols
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          if (j < v) {
-            uint32_t c, f;
-            model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), s[j], c, f);
-            cod.encode(c, f);
-          }
-        }
+      for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
+      if (b + 1 < nfull) nxt.load_full(a, base + lane + (int64_t)(b + 1) * kStep);  // in flight meanwhile
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        uint32_t c, f;
+        model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), s[j], c, f);
+        cod.encode(c, f);
       }
       cur = nxt;
+    }
+    // the last, partial batch of a short chunk: symbol by symbol
+    for (int k = nfull * kBatch; k < nk; ++k) {
+      const int64_t i = base + lane + (int64_t)k * kLanes;
+      const int j = k & (kBatch - 1);
+      float sj = s[0];
+#pragma unroll
+      for (int q = 1; q < kBatch; ++q)
+        if (j == q) sj = s[q];
+      cur.one(a, i, 0);
+      uint32_t c, f;
+      model_pair<SYM, FAST>(a, t, cur.xs[0], cur.mu(0), sj, c, f);
+      cod.encode(c, f);
     }
     uint32_t nbytes = cod.finish();
     // every frequency >= 1 bounds a lane at 3 bytes per symbol + 1; more means a broken table
