@@ -56,7 +56,7 @@ int make_geo(const skv_shape *sh, Geo &g) {
 }
 
 struct Layout {
-  size_t knots, ptab, a16, abase, aflag, uinv, etab, scale, lens, sizes, scratch, total;
+  size_t knots, ptab, a16, abase, aflag, psum, uinv, etab, scale, lens, sizes, scratch, total;
 };
 
 Layout layout(const Geo &g) {
@@ -67,6 +67,7 @@ Layout layout(const Geo &g) {
   L.a16 = o;   o = align_up(o + sizeof(uint16_t) * kNWin * kWinEntries);
   L.abase = o; o = align_up(o + sizeof(uint32_t) * (kNWin + 1));
   L.aflag = o; o = align_up(o + sizeof(int32_t));
+  L.psum = o;  o = align_up(o + sizeof(uint64_t) * 64);
   L.uinv = o;  o = align_up(o + sizeof(float2) * (kNInv + 1));
   L.etab = o;  o = align_up(o + sizeof(float2) * 256);
   L.scale = o; o = align_up(o + sizeof(float2) * (size_t)(g.rows * g.D));
@@ -86,6 +87,7 @@ Workspace carve(const Geo &g, void *base) {
   w.a16 = reinterpret_cast<uint16_t *>(b + L.a16);
   w.abase = reinterpret_cast<uint32_t *>(b + L.abase);
   w.aflag = reinterpret_cast<int32_t *>(b + L.aflag);
+  w.psum = reinterpret_cast<uint64_t *>(b + L.psum);
   w.uinv = reinterpret_cast<float2 *>(b + L.uinv);
   w.etab = reinterpret_cast<float2 *>(b + L.etab);
   w.scale = reinterpret_cast<float2 *>(b + L.scale);

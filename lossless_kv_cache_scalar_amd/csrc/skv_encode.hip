@@ -70,16 +70,22 @@ struct LaneCoder {
   uint64_t X, range, acc;
   int nbits;
   uint32_t nw, capw;
-  uint32_t *out;
+  uint32_t *out;   // the lane's word 0 in the chunk's slot
+  uint8_t *slot;   // the chunk's slot (the same for the whole wave)
+  uint32_t off;    // byte offset of word min(nw, capw - 1) in the slot
+  uint32_t offmax;
 
-  __device__ __forceinline__ void init(uint32_t *o, uint32_t cap_words) {
+  __device__ __forceinline__ void init(uint8_t *chunk_slot, uint32_t lane, uint32_t cap_words) {
     X = 0;
     range = kW48;
     acc = 0;
     nbits = -16;
     nw = 0;
     capw = cap_words;
-    out = o;
+    slot = chunk_slot;
+    out = reinterpret_cast<uint32_t *>(chunk_slot) + lane;
+    off = 4u * lane;
+    offmax = 4u * ((cap_words - 1) * kLanes + lane);
   }
 
   // Stores the word that starts at bit nbits - 32 of acc on every symbol, so
@@ -89,22 +95,22 @@ struct LaneCoder {
   // rewrites its last word.
   __device__ __forceinline__ void flush_word() {
     const uint32_t word = (uint32_t)(acc >> ((nbits - 32) & 63));
-    out[min(nw, capw - 1) * kLanes] = __builtin_bswap32(word);
+    *reinterpret_cast<uint32_t *>(slot + off) = __builtin_bswap32(word);
     if (nbits >= 32) {
       ++nw;
       nbits -= 32;
+      off = min(off + 4u * kLanes, offmax);
     }
   }
 
   // c, f on the coder's 2^24 total (f >= 1)
   __device__ __forceinline__ void encode(uint32_t c, uint32_t f) {
-    const uint32_t r = (uint32_t)(range >> 24);
+    const uint32_t r = (uint32_t)(range >> 24);  // range < 2^48
+    __builtin_assume(r < (1u << 24));
     const uint64_t p = mul24(r, c);
-    unsigned int c0, c1;
-    const uint32_t xl = __builtin_addc((uint32_t)X, (uint32_t)p, 0u, &c0);
-    const uint32_t xh = __builtin_addc((uint32_t)(X >> 32), (uint32_t)(p >> 32), c0, &c1);
-    X = ((uint64_t)xh << 32) | xl;
-    const bool carry = c1 != 0;
+    const uint64_t Xn = X + p;
+    const bool carry = Xn < p;  // out of bit 63
+    X = Xn;
     const uint64_t rg = mul24(r, f);
     const uint32_t n8 = __builtin_clz((uint32_t)(rg >> 16)) & ~7u;  // bytes to shift, x8
     if (__builtin_expect(__any(carry), 0)) {
@@ -230,7 +236,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(s[j]));
 
     LaneCoder cod;
-    cod.init(reinterpret_cast<uint32_t *>(a.scratch + (uint64_t)chunk * kLanes * g.lane_cap) + lane, g.lane_cap / 4);
+    cod.init(a.scratch + (uint64_t)chunk * kLanes * g.lane_cap, (uint32_t)lane, g.lane_cap / 4);
 
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;  // this lane's symbols
     const int nfull = nsc / kStep;                                         // batches every lane fills

@@ -61,6 +61,7 @@ struct Workspace {
   uint16_t *a16;      // kNWin * kWinEntries: A(64w + j) - A(64w) (bf16)
   uint32_t *abase;    // kNWin + 1: A(64w)
   int32_t *aflag;     // 1 when every window's offsets fit 16 bits
+  uint64_t *psum;     // per 1024 ranks: sum of hist + 1 (table build)
   float2 *uinv;       // kNInv + 1: (u, du) at y = m * MG / kNInv
   float2 *etab;       // 256 e4m3 bins (lo, hi), indexed by pattern
   float2 *scale;      // per channel: (s, ~1/s), s = RN32(64 / max(sigma, 2^-100))

@@ -57,70 +57,92 @@ __device__ __forceinline__ uint64_t floor_div(uint64_t num, uint64_t den) {
   return q;
 }
 
-// One block of 1024 threads; thread t owns window t: ranks 64t .. 64t + 63
-// (bf16: all 1024 windows; e4m3: the first 4).  Writes the full table A and,
-// for bf16, the LDS image: base A(64t) and 65 u16 offsets A(64t + j) - A(64t),
-// j = 0..64, flagging a window whose offsets do not fit 16 bits.
-__global__ __launch_bounds__(1024) void k_ptable(const uint64_t *__restrict__ hist, uint32_t *__restrict__ A,
-                                                 uint16_t *__restrict__ a16, uint32_t *__restrict__ abase,
-                                                 int32_t *__restrict__ aflag, uint32_t N, uint32_t Mp, int bf16,
-                                                 int32_t *status) {
-  __shared__ uint64_t part[1024];
-  __shared__ int bad, narrow;
-  const int t = threadIdx.x;
-  const uint32_t nwin = N / kWinRanks;
-  const bool active = (uint32_t)t < nwin;
-  const uint32_t k0 = (uint32_t)t * kWinRanks;
+// Two kernels, one thread per rank, 1024 ranks per block.  k_psums: the
+// counts hist[unrank k] + 1 of each block, summed.  k_ptable: H(k) from the
+// block sums and a block scan, then A(k); for bf16 also the LDS image of the
+// table: window w's base A(64 w) and 65 u16 offsets A(64 w + j) - A(64 w),
+// j = 0..64, clearing aflag when some window's offsets do not fit 16 bits.
+constexpr int kPtBlock = 1024;
+
+__device__ __forceinline__ uint64_t rank_count(const uint64_t *__restrict__ hist, uint32_t k, int bf16) {
+  return hist[bf16 ? unrank_bf16(k) : unrank_e4m3(k)] + 1;
+}
+
+__device__ __forceinline__ uint64_t block_sum(uint64_t v, uint64_t *red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
   uint64_t s = 0;
-  if (active)
-    for (int j = 0; j < kWinRanks; ++j) {
-      uint32_t k = k0 + j;
-      s += hist[bf16 ? unrank_bf16(k) : unrank_e4m3(k)] + 1;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+  return s;
+}
+
+__global__ __launch_bounds__(kPtBlock) void k_psums(const uint64_t *__restrict__ hist, uint64_t *__restrict__ psum,
+                                                    int32_t *__restrict__ aflag, uint32_t N, int bf16) {
+  __shared__ uint64_t red[kPtBlock / 64];
+  const uint32_t k = blockIdx.x * kPtBlock + threadIdx.x;
+  const uint64_t s = block_sum(k < N ? rank_count(hist, k, bf16) : 0, red);
+  if (threadIdx.x == 0) psum[blockIdx.x] = s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *aflag = bf16 ? 1 : 0;
+}
+
+__global__ __launch_bounds__(kPtBlock) void k_ptable(const uint64_t *__restrict__ hist,
+                                                     const uint64_t *__restrict__ psum, uint32_t *__restrict__ A,
+                                                     uint16_t *__restrict__ a16, uint32_t *__restrict__ abase,
+                                                     int32_t *__restrict__ aflag, uint32_t N, uint32_t Mp, int bf16,
+                                                     int32_t *status) {
+  __shared__ uint64_t scan[kPtBlock];
+  const int t = threadIdx.x;
+  const uint32_t nblk = gridDim.x;
+  // the total and this block's base from the block sums
+  uint64_t base = 0, total = 0;
+  for (uint32_t i = 0; i < nblk; ++i) {
+    const uint64_t v = psum[i];
+    if (i < blockIdx.x) base += v;
+    total += v;
+  }
+  const uint32_t k = blockIdx.x * kPtBlock + t;
+  const bool active = k < N;
+  const uint64_t c = active ? rank_count(hist, k, bf16) : 0;
+  scan[t] = c;
+  __syncthreads();
+  for (int off = 1; off < kPtBlock; off <<= 1) {
+    const uint64_t v = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  const uint64_t H = base + scan[t] - c;  // H(k), exclusive
+  if (total < N || (Mp != 0 && total > (1ull << 62) / Mp)) {  // uniform table: every frequency stays >= 1
+    if (blockIdx.x == 0 && t == 0) {
+      set_status(status, SKV_ERR_TABLE);
+      *aflag = 0;
     }
-  part[t] = s;
-  if (t == 0) {
-    bad = 0;
-    narrow = 0;
-  }
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    uint64_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  const uint64_t total = part[1023];
-  uint64_t H = part[t] - s;  // exclusive prefix
-  if (t == 0 && (total < N || (Mp != 0 && total > (1ull << 62) / Mp))) bad = 1;
-  __syncthreads();
-  if (bad) {  // uniform table so that every frequency stays >= 1
-    if (t == 0) set_status(status, SKV_ERR_TABLE);
-    for (uint32_t k = t; k <= N; k += blockDim.x) A[k] = k + (uint32_t)(((uint64_t)Mp * k) / N);
-    if (t == 0) *aflag = 0;
+    if (active) A[k] = k + (uint32_t)(((uint64_t)Mp * k) / N);
+    if (k == N - 1) A[N] = N + Mp;
     return;
   }
-  if (active) {
-    uint32_t a0 = 0;
-    for (int j = 0; j <= kWinRanks; ++j) {
-      const uint32_t k = k0 + j;
-      uint32_t ak = k + (uint32_t)floor_div((uint64_t)Mp * H, total);
-      if (j < kWinRanks) A[k] = ak;
-      if (j == 0) a0 = ak;
-      if (bf16) {
-        uint32_t off = ak - a0;
-        if (off > 0xFFFFu) atomicOr(&narrow, 1);
-        a16[t * kWinEntries + j] = (uint16_t)off;
-      }
-      if (j < kWinRanks) H += hist[bf16 ? unrank_bf16(k) : unrank_e4m3(k)] + 1;
-    }
-    if (bf16) abase[t] = a0;
+  if (!active) return;
+  const uint32_t ak = k + (uint32_t)floor_div((uint64_t)Mp * H, total);
+  A[k] = ak;
+  if (k == N - 1) A[N] = N + Mp;
+  if (!bf16) return;
+  // window image: thread j = 0 of a window holds its base; j = 63 also writes
+  // entry 64, A(64 w + 64) - A(64 w)
+  const uint32_t w = k / kWinRanks, j = k % kWinRanks;
+  const uint32_t a0 = __shfl(ak, 0, 64);  // the window is this wave
+  if (j == 0) abase[w] = ak;
+  uint32_t off = ak - a0;
+  bool wide = off > 0xFFFFu;
+  a16[w * kWinEntries + j] = (uint16_t)off;
+  if (j == kWinRanks - 1) {
+    const uint32_t an = k + 1 + (uint32_t)floor_div((uint64_t)Mp * (H + c), total);
+    const uint32_t on = an - a0;
+    wide = wide || on > 0xFFFFu;
+    a16[w * kWinEntries + kWinRanks] = (uint16_t)on;
+    if (w == N / kWinRanks - 1) abase[w + 1] = an;
   }
-  __syncthreads();
-  if (t == 0) {
-    A[N] = N + Mp;
-    if (bf16) abase[nwin] = N + Mp;
-    *aflag = bf16 && !narrow ? 1 : 0;
-  }
+  if (__any(wide) && j == 0) atomicAnd(aflag, 0);
 }
 
 // ---------------------------------------------------------------- inverse CDF
@@ -202,8 +224,11 @@ hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, 
                         int32_t *status, hipStream_t st) {
   timing_mark(kTimeModel, false, st);
   hipLaunchKernelGGL(k_knots, dim3(1), dim3(1024), 0, st, ws.knots, g.MG);
-  hipLaunchKernelGGL(k_ptable, dim3(1), dim3(1024), 0, st, hist, ws.ptab, ws.a16, ws.abase, ws.aflag, g.N, g.Mp,
-                     g.sym_fmt == SKV_SYM_BF16 ? 1 : 0, status);
+  const unsigned pblocks = (g.N + kPtBlock - 1) / kPtBlock;
+  const int bf = g.sym_fmt == SKV_SYM_BF16 ? 1 : 0;
+  hipLaunchKernelGGL(k_psums, dim3(pblocks), dim3(kPtBlock), 0, st, hist, ws.psum, ws.aflag, g.N, bf);
+  hipLaunchKernelGGL(k_ptable, dim3(pblocks), dim3(kPtBlock), 0, st, hist, ws.psum, ws.ptab, ws.a16, ws.abase,
+                     ws.aflag, g.N, g.Mp, bf, status);
   hipLaunchKernelGGL(k_uinv, dim3(1), dim3(1024), 0, st, ws.knots, ws.uinv, g.MG);
   if (g.sym_fmt == SKV_SYM_E4M3) hipLaunchKernelGGL(k_etab, dim3(1), dim3(256), 0, st, ws.etab);
   int64_t nch = g.rows * g.D;
