@@ -180,7 +180,7 @@ int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bits_bytes,
 /*
  * Measurement aid, not part of the method.  Between skv_timing_start and
  * skv_timing_stop every main launch of skv_encode / skv_decode (the model
- * build as one record, k_encode, k_offsets, k_compact, k_decode) is bracketed
+ * build as one record, k_encode, k_decode) is bracketed
  * by two HIP events recorded on the call's own stream, so one kernel's time is
  * known without a profiler and without synchronising between calls.
  * Recording is process-wide and meant for one host thread issuing the calls.
@@ -195,7 +195,7 @@ int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bits_bytes,
  *   events and stops recording.  SKV_ERR_ARG if recording is off or a pointer
  *   is null; SKV_ERR_HIP if an event could not be read (its time is 0).
  * skv_timed_kernel_name: the name of a kernel id ("model", "k_encode",
- *   "k_offsets", "k_compact", "k_decode"; "unknown" otherwise), static storage.
+ *   "k_decode"; "unknown" otherwise), static storage.
  */
 int skv_timing_start(int32_t capacity);
 int skv_timing_stop(int32_t *kernel, float *ms, int32_t capacity, int32_t *count);

@@ -56,7 +56,7 @@ int make_geo(const skv_shape *sh, Geo &g) {
 }
 
 struct Layout {
-  size_t knots, ptab, a16, abase, aflag, psum, uinv, etab, scale, lens, sizes, scratch, total;
+  size_t knots, ptab, a16, abase, aflag, psum, uinv, etab, scale, flags, ctr, scratch, total;
 };
 
 Layout layout(const Geo &g) {
@@ -71,8 +71,8 @@ Layout layout(const Geo &g) {
   L.uinv = o;  o = align_up(o + sizeof(float2) * (kNInv + 1));
   L.etab = o;  o = align_up(o + sizeof(float2) * 256);
   L.scale = o; o = align_up(o + sizeof(float2) * (size_t)(g.rows * g.D));
-  L.lens = o;  o = align_up(o + sizeof(uint32_t) * (size_t)g.n_chunks * kLanes);
-  L.sizes = o; o = align_up(o + sizeof(uint64_t) * (size_t)g.n_chunks);
+  L.flags = o; o = align_up(o + sizeof(uint64_t) * (size_t)g.n_chunks);
+  L.ctr = o;   o = align_up(o + sizeof(uint32_t));
   L.scratch = o; o = align_up(o + (size_t)g.n_chunks * kLanes * g.lane_cap);
   L.total = o;
   return L;
@@ -91,8 +91,8 @@ Workspace carve(const Geo &g, void *base) {
   w.uinv = reinterpret_cast<float2 *>(b + L.uinv);
   w.etab = reinterpret_cast<float2 *>(b + L.etab);
   w.scale = reinterpret_cast<float2 *>(b + L.scale);
-  w.lens = reinterpret_cast<uint32_t *>(b + L.lens);
-  w.sizes = reinterpret_cast<uint64_t *>(b + L.sizes);
+  w.flags = reinterpret_cast<uint64_t *>(b + L.flags);
+  w.ctr = reinterpret_cast<uint32_t *>(b + L.ctr);
   w.scratch = b + L.scratch;
   return w;
 }

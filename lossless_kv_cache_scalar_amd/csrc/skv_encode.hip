@@ -10,9 +10,13 @@
 // Each lane writes its substream as whole 32-bit words into the chunk's
 // scratch slot, word w of lane l at word 64 w + l: a wave's stores land side
 // by side, and the first m words of every lane already sit in the stream's
-// interleaved layout.  A scan over chunk sizes gives the offsets; a compaction
-// kernel writes each chunk (length header, interleaved words, the lanes'
-// remaining bytes, padding) at its offset.
+// interleaved layout.  Chunk ids come from an atomic counter in increasing
+// order; a finished chunk publishes its size, finds its offset by looking back
+// over its predecessors' published sizes and prefixes (a single-pass scan:
+// every chunk it waits for was taken earlier by a running wave, so the lowest
+// unfinished chunk never waits), and its wave then writes the chunk (length
+// header, interleaved words, the lanes' remaining bytes, padding) at that
+// offset.
 #include "skv_internal.hpp"
 
 namespace skv {
@@ -30,11 +34,120 @@ struct EncArgs {
   const int32_t *aflag;
   const float2 *etab;
   const float2 *scale;
-  uint32_t *lens;
-  uint64_t *sizes;
+  uint64_t *flags;  // per chunk: kFlagAgg | size, then kFlagIncl | offset + size
+  uint32_t *ctr;    // next chunk id
   uint8_t *scratch;
+  uint8_t *bits;
+  uint64_t bits_cap;
+  uint64_t *offsets;
   int32_t *status;
 };
+
+// chunk status words of the single-pass scan (0: not yet published)
+constexpr uint64_t kFlagAgg = 1ull << 62;   // the chunk's own size
+constexpr uint64_t kFlagIncl = 2ull << 62;  // its offset + size
+constexpr uint64_t kFlagVal = kFlagAgg - 1;
+constexpr uint32_t kSpinLimit = 1u << 20;   // polls of one predecessor before giving up
+
+__device__ __forceinline__ uint64_t flag_load(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Offset of chunk c (> 0) from the published words of its predecessors: lane
+// l reads chunks p - l - 64 u, u < kLookBack; the nearest inclusive prefix ends
+// the walk, aggregates before it add up.  Returns false when the nearest
+// unpublished predecessor is still unpublished after max_spins polls.
+constexpr int kLookBack = 8;
+__device__ bool look_back(const uint64_t *flags, int64_t c, int lane, uint64_t &excl, uint32_t max_spins) {
+  excl = 0;
+  int64_t p = c - 1;  // the nearest chunk not yet accounted for
+  uint32_t spins = 0;
+  for (;;) {
+    uint64_t f[kLookBack];
+#pragma unroll
+    for (int u = 0; u < kLookBack; ++u) {
+      const int64_t q = p - lane - (int64_t)kLanes * u;
+      f[u] = q >= 0 ? flag_load(flags + q) : kFlagIncl;  // before chunk 0: offset 0
+    }
+    bool wait = false;
+#pragma unroll
+    for (int u = 0; u < kLookBack; ++u) {
+      if (wait) break;
+      const uint64_t st = f[u] >> 62;
+      const uint64_t stop = __ballot(st != 1);
+      if (stop == 0) {  // 64 aggregates
+        excl += wave_sum64(f[u] & kFlagVal);
+        p -= kLanes;
+        continue;
+      }
+      const int first = __builtin_ctzll(stop);  // the nearest chunk not holding a plain aggregate
+      const uint64_t stf = __shfl(st, first, 64);
+      excl += wave_sum64(lane < first || (stf == 2 && lane == first) ? (f[u] & kFlagVal) : 0);
+      if (stf == 2) return true;
+      p -= first;  // chunk p has not published yet
+      wait = true;
+    }
+    if (wait) {
+      if (spins++ >= max_spins) return false;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+}
+
+// Chunk c's bytes at bits[o0, o0 + size): the header, the interleaved words
+// (copied as they sit in the slot), each lane's remaining bytes, zeros.
+__device__ __forceinline__ void write_chunk(uint8_t *__restrict__ bits, uint64_t o0, uint64_t size,
+                                            const uint8_t *slot, uint32_t len, int lane) {
+  reinterpret_cast<uint16_t *>(bits + o0)[lane] = (uint16_t)len;
+  uint32_t m = len >> 2;
+  for (int off = 32; off > 0; off >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  const uint32_t tail = len - 4 * m;
+  uint32_t inc = tail;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += v;
+  }
+  const uint32_t tails = __shfl(inc, 63, 64);
+  const uint32_t *sw = reinterpret_cast<const uint32_t *>(slot);
+  uint32_t *dw = reinterpret_cast<uint32_t *>(bits + o0 + kHeaderBytes);
+  // 16 loads in flight per lane, then their stores
+  constexpr int kCopy = 16;
+  const uint32_t nwords = kLanes * m;
+  for (uint32_t q0 = 0; q0 < nwords; q0 += kLanes * kCopy) {
+    uint32_t v[kCopy];
+#pragma unroll
+    for (int u = 0; u < kCopy; ++u) {
+      const uint32_t q = q0 + kLanes * u + (uint32_t)lane;
+      v[u] = q < nwords ? sw[q] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kCopy; ++u) {
+      const uint32_t q = q0 + kLanes * u + (uint32_t)lane;
+      if (q < nwords) dw[q] = v[u];
+    }
+  }
+  // the lane's remaining bytes: its words m, m + 1, ... four at a time
+  const uint64_t d0 = o0 + kHeaderBytes + 4ull * kLanes * m + (inc - tail);
+  for (uint32_t j0 = 0; j0 < tail; j0 += 16) {
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = j0 + 4u * u < tail ? sw[(m + (j0 >> 2) + u) * kLanes + (uint32_t)lane] : 0u;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (j0 + u < tail) bits[d0 + j0 + u] = (uint8_t)(v[u >> 2] >> (8 * (u & 3)));
+  }
+  const uint64_t end = o0 + kHeaderBytes + 4ull * kLanes * m + tails;
+  if (lane < 3 && end + lane < o0 + size) bits[end + lane] = 0;
+}
 
 // exact 48-bit product of two values below 2^24: v_mul_u32_u24 + v_mul_hi_u32_u24
 __device__ __forceinline__ uint64_t mul24(uint32_t a, uint32_t b) {
@@ -218,8 +331,39 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
   const int wave = threadIdx.x >> 6;
   const int D = (int)g.D;
   constexpr int kStep = kLanes * kBatch;  // scalars of one batch of the wave
-  for (int64_t chunk = (int64_t)blockIdx.x * kEncWaves + wave; chunk < g.n_chunks;
-       chunk += (int64_t)gridDim.x * kEncWaves) {
+  (void)wave;
+  // A chunk whose look-back would have to wait is finished after the wave has
+  // coded its next chunk: by then its predecessors have published.
+  int64_t pend = -1;
+  uint32_t pend_len = 0;
+  uint64_t pend_size = 0;
+  auto finalize = [&](int64_t c, uint64_t o0, uint64_t size, uint32_t len) {
+    if (lane == 0) {
+      flag_store(a.flags + c, kFlagIncl | (o0 + size));
+      a.offsets[c] = o0;
+      if (c == g.n_chunks - 1) {
+        a.offsets[c + 1] = o0 + size;
+        if (o0 + size > a.bits_cap) set_status(a.status, SKV_ERR_CAPACITY);
+      }
+    }
+    // the slot was written by this wave: its stores are complete and visible to
+    // its own loads after a workgroup-scope fence (no cache writeback needed)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    if (o0 + size <= a.bits_cap)
+      write_chunk(a.bits, o0, size, a.scratch + (uint64_t)c * kLanes * g.lane_cap, len, lane);
+  };
+  for (;;) {
+    uint32_t cid = 0;
+    if (lane == 0) cid = atomicAdd(a.ctr, 1u);
+    const int64_t chunk = (int64_t)__builtin_amdgcn_readfirstlane(__shfl(cid, 0, 64));  // uniform: kept in SGPRs
+    if (chunk >= g.n_chunks) {
+      if (pend >= 0) {
+        uint64_t o0;
+        if (!look_back(a.flags, pend, lane, o0, kSpinLimit)) set_status(a.status, SKV_ERR_HIP);
+        finalize(pend, o0, pend_size, pend_len);
+      }
+      break;
+    }
     const int64_t row = chunk / g.ntb, blk = chunk - row * g.ntb;
     const int64_t tok = min<int64_t>(kChunkTokens, g.tokens - blk * kChunkTokens);
     const int nsc = (int)(tok * D);
@@ -279,10 +423,31 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
       set_status(a.status, SKV_ERR_TABLE);
       nbytes = g.lane_cap;
     }
-    a.lens[chunk * kLanes + lane] = nbytes;
     uint32_t tot = nbytes;
     for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
-    if (lane == 0) a.sizes[chunk] = ((uint64_t)kHeaderBytes + tot + 3) & ~3ull;
+    const uint64_t size = ((uint64_t)kHeaderBytes + tot + 3) & ~3ull;
+
+    // ---- offsets: publish the size; finish the pending chunk, then this one
+    // unless it would have to wait
+    if (chunk == 0) {
+      finalize(0, 0, size, nbytes);
+      continue;
+    }
+    if (lane == 0) flag_store(a.flags + chunk, kFlagAgg | size);
+    if (pend >= 0) {
+      uint64_t o0;
+      if (!look_back(a.flags, pend, lane, o0, kSpinLimit)) set_status(a.status, SKV_ERR_HIP);
+      finalize(pend, o0, pend_size, pend_len);
+      pend = -1;
+    }
+    uint64_t o0;
+    if (look_back(a.flags, chunk, lane, o0, 0)) {
+      finalize(chunk, o0, size, nbytes);
+    } else {
+      pend = chunk;
+      pend_len = nbytes;
+      pend_size = size;
+    }
   }
 }
 
@@ -312,82 +477,10 @@ __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   else encode_chunks<SYM, MU, false>(a, t);
 }
 
-// ---- exclusive scan of chunk sizes into offsets (one block) ----
-__global__ __launch_bounds__(1024) void k_offsets(const uint64_t *__restrict__ sizes, uint64_t *__restrict__ offsets,
-                                                  int64_t n, uint64_t cap, int32_t *status) {
-  __shared__ uint64_t part[1024];
-  const int t = threadIdx.x;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t i0 = t * per, i1 = min<int64_t>(n, i0 + per);
-  uint64_t s = 0;
-  for (int64_t i = i0; i < i1; ++i) s += sizes[i];
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    uint64_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  uint64_t run = part[t] - s;
-  for (int64_t i = i0; i < i1; ++i) {
-    offsets[i] = run;
-    run += sizes[i];
-  }
-  if (t == 1023) {
-    offsets[n] = part[1023];
-    if (part[1023] > cap) set_status(status, SKV_ERR_CAPACITY);
-  }
-}
-
-// ---- compaction: one block per chunk ----
-// Chunk c occupies [o0, o1) of the stream, o0 a multiple of 4: the u16 length
-// header; the first m words of every lane, already interleaved in the scratch
-// slot (word w of lane l at word 64 w + l), copied as they are; each lane's
-// remaining len - 4m bytes, lane after lane; zeros up to o1.
-__global__ __launch_bounds__(256) void k_compact(const uint32_t *__restrict__ lens_g, const uint8_t *__restrict__ scratch,
-                                                 const uint64_t *__restrict__ offsets, uint8_t *__restrict__ bits,
-                                                 uint64_t cap, uint32_t lane_cap) {
-  __shared__ uint32_t s_tail[kLanes + 1];  // exclusive prefix of the lanes' remaining bytes
-  __shared__ uint32_t s_m;
-  const int64_t chunk = blockIdx.x;
-  const uint64_t o0 = offsets[chunk], o1 = offsets[chunk + 1];
-  if (o1 > cap) return;  // capacity error already recorded; write nothing past the buffer
-  const int t = threadIdx.x;
-  const uint8_t *src = scratch + (uint64_t)chunk * kLanes * lane_cap;
-  if (t < kLanes) {
-    const uint32_t len = lens_g[chunk * kLanes + t];
-    reinterpret_cast<uint16_t *>(bits + o0)[t] = (uint16_t)len;
-    uint32_t m = len >> 2;
-    for (int off = 32; off > 0; off >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    uint32_t inc = len - 4 * m;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(inc, off, 64);
-      if (t >= off) inc += v;
-    }
-    s_tail[t + 1] = inc;
-    if (t == 0) {
-      s_tail[0] = 0;
-      s_m = m;
-    }
-  }
-  __syncthreads();
-  const uint32_t m = s_m;
-  const uint32_t *sw = reinterpret_cast<const uint32_t *>(src);
-  uint32_t *dw = reinterpret_cast<uint32_t *>(bits + o0 + kHeaderBytes);
-  for (uint32_t q = t; q < kLanes * m; q += 256) dw[q] = sw[q];
-  // the rest of lane l: 4 threads per lane, byte j of the tail is byte 4m + j of the lane
-  const int l = t & 63;
-  const uint64_t d0 = o0 + kHeaderBytes + 4ull * kLanes * m + s_tail[l];
-  const uint32_t n = s_tail[l + 1] - s_tail[l];
-  for (uint32_t j = (uint32_t)(t >> 6); j < n; j += 4) {
-    const uint32_t wi = m + (j >> 2);
-    bits[d0 + j] = src[4u * (wi * kLanes + (uint32_t)l) + (j & 3u)];
-  }
-  if (t < 3) {
-    const uint64_t end = o0 + kHeaderBytes + 4ull * kLanes * m + s_tail[kLanes];
-    if (end + t < o1) bits[end + t] = 0;
-  }
+__global__ void k_enc_reset(uint64_t *__restrict__ flags, int64_t n, uint32_t *__restrict__ ctr) {
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t i = i0; i < n; i += (int64_t)gridDim.x * blockDim.x) flags[i] = 0;
+  if (i0 == 0) *ctr = 0;
 }
 
 static int cu_count() {
@@ -411,8 +504,9 @@ static void launch_enc_kernel(const EncArgs &a, hipStream_t st) {
 
 hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Workspace &ws, uint8_t *bits,
                          uint64_t bits_cap, uint64_t *offsets, int32_t *status, hipStream_t st) {
-  EncArgs a{g, x, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.etab, ws.scale, ws.lens, ws.sizes,
-            ws.scratch, status};
+  EncArgs a{g, x, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.etab, ws.scale, ws.flags, ws.ctr,
+            ws.scratch, bits, bits_cap, offsets, status};
+  hipLaunchKernelGGL(k_enc_reset, dim3(256), dim3(256), 0, st, ws.flags, g.n_chunks, ws.ctr);
   timing_mark(kTimeEncode, false, st);
   if (g.sym_fmt == SKV_SYM_BF16) {
     if (g.mu_fmt == SKV_MU_BF16) launch_enc_kernel<SKV_SYM_BF16, SKV_MU_BF16>(a, st);
@@ -422,13 +516,6 @@ hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Work
     else launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_F32>(a, st);
   }
   timing_mark(kTimeEncode, true, st);
-  timing_mark(kTimeOffsets, false, st);
-  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, st, ws.sizes, offsets, g.n_chunks, bits_cap, status);
-  timing_mark(kTimeOffsets, true, st);
-  timing_mark(kTimeCompact, false, st);
-  hipLaunchKernelGGL(k_compact, dim3((unsigned)g.n_chunks), dim3(256), 0, st, ws.lens, ws.scratch, offsets, bits,
-                     bits_cap, g.lane_cap);
-  timing_mark(kTimeCompact, true, st);
   return hipGetLastError();
 }
 

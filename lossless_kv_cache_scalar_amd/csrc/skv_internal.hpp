@@ -51,7 +51,7 @@ struct Geo {
 // Optional per-kernel timing (skv_timing_start .. skv_timing_stop): while it
 // is on, timing_mark records a HIP event on `st` before (end = false) and after
 // (end = true) each main launch.
-enum TimedKernel { kTimeModel = 0, kTimeEncode, kTimeOffsets, kTimeCompact, kTimeDecode, kTimeCount };
+enum TimedKernel { kTimeModel = 0, kTimeEncode, kTimeDecode, kTimeCount };
 void timing_mark(int kernel, bool end, hipStream_t st);
 
 // ---- workspace layout (encode and decode share it) ----
@@ -65,8 +65,8 @@ struct Workspace {
   float2 *uinv;       // kNInv + 1: (u, du) at y = m * MG / kNInv
   float2 *etab;       // 256 e4m3 bins (lo, hi), indexed by pattern
   float2 *scale;      // per channel: (s, ~1/s), s = RN32(64 / max(sigma, 2^-100))
-  uint32_t *lens;     // n_chunks * 64 substream lengths (encode)
-  uint64_t *sizes;    // n_chunks chunk sizes (encode)
+  uint64_t *flags;    // n_chunks published sizes / prefixes (encode)
+  uint32_t *ctr;      // next chunk id (encode)
   uint8_t *scratch;   // n_chunks * 64 * lane_cap (encode)
 };
 

@@ -94,8 +94,6 @@ extern "C" const char *skv_timed_kernel_name(int32_t kernel) {
   switch (kernel) {
     case kTimeModel: return "model";
     case kTimeEncode: return "k_encode";
-    case kTimeOffsets: return "k_offsets";
-    case kTimeCompact: return "k_compact";
     case kTimeDecode: return "k_decode";
     default: return "unknown";
   }

@@ -73,5 +73,5 @@ def test_timing_argument_checks(lib):
     assert lib.skv_timing_start((1 << 20) + 1) == skv.ERR_ARG
     assert lib.skv_timing_stop(None, None, 0, C.byref(n)) == skv.ERR_ARG  # not recording
     assert lib.skv_timing_stop(None, None, 4, C.byref(n)) == skv.ERR_ARG
-    names = [skv.load().skv_timed_kernel_name(i).decode() for i in range(6)]
-    assert names == ["model", "k_encode", "k_offsets", "k_compact", "k_decode", "unknown"]
+    names = [skv.load().skv_timed_kernel_name(i).decode() for i in range(4)]
+    assert names == ["model", "k_encode", "k_decode", "unknown"]
