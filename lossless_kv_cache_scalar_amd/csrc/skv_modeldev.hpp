@@ -111,7 +111,15 @@ template <int SYM, int TAB>
 __device__ __forceinline__ uint32_t cum_rank(const ModelTabs &t, uint32_t k, float m, float s) {
   if (SYM == SKV_SYM_BF16) {
     if (k >= 65536u) return 1u << 24;
-    return a_one<TAB>(t, k) + cg_eval(t.kn, u_of(bf16_lo_edge(unrank_bf16(k)), m, s));
+    // lower edge of a finite non-zero b: half an ulp below (b > 0) or above
+    // (b < 0) in fp32 bits; +-0, +-inf and NaN take the general edge
+    const uint32_t b = unrank_bf16(k);
+    uint32_t e = (b & 0x8000u) ? ((b << 16) | 0x8000u) : ((b << 16) - 0x8000u);
+    const bool special = ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17);
+    if (__builtin_expect(__any(special), 0)) {
+      if (special) e = __float_as_uint(bf16_lo_edge(b));
+    }
+    return a_one<TAB>(t, k) + cg_eval(t.kn, u_of(__uint_as_float(e), m, s));
   } else {
     if (k >= 256u) return 1u << 16;
     return t.ab[k] + cg_eval(t.kn, u_of(t.et[unrank_e4m3(k)].x, m, s));
