@@ -19,6 +19,12 @@ cache geometry stands in for them:
   format (bf16, or kept fp32);
 * FP8 caches code e4m3(x) (round to nearest even, saturating at +-448).
 
+A second kind of predictor stands in for the FP8 model's own cache ("同一模型
+的优化版本": the predictor is a quantized copy of the same model): mu is the
+block-FP8 round trip of x itself, with one fp32 scale per 32 consecutive
+channels of a token (amax / 448), so the residual is bounded, structured
+rounding noise rather than the mixture above.
+
 Layout of x and mu: [layers][2 (K, V)][kv_heads][tokens][head_dim].
 Symbols are returned as raw bit patterns (uint16 for bf16, uint8 for e4m3);
 bf16 predictor means as uint16 bit patterns, fp32 ones as float32.
@@ -46,6 +52,7 @@ class Workload:
     sigma_k: float        # sigma_c = sigma_k * s_c
     calib_seqs: int
     calib_tokens: int
+    mu_kind: str = "mixture"  # "mixture": x + sigma_c r; "fp8block": block-FP8 round trip of x
 
     @property
     def model_seed(self) -> int:
@@ -76,7 +83,8 @@ class Workload:
 
     def with_tokens(self, tokens: int, layers: int | None = None, name: str | None = None) -> "Workload":
         return Workload(name or self.name, self.index, layers or self.layers, self.kv_heads, self.head_dim,
-                        tokens, self.sym_fmt, self.mu_fmt, self.sigma_k, self.calib_seqs, self.calib_tokens)
+                        tokens, self.sym_fmt, self.mu_fmt, self.sigma_k, self.calib_seqs, self.calib_tokens,
+                        self.mu_kind)
 
 
 WORKLOADS = {
@@ -92,6 +100,8 @@ WORKLOADS = {
         Workload("qwen3_32b_bf16", 4, 64, 8, 128, 8192, SYM_BF16, MU_BF16, 0.015, 128, 512),
         # Qwen3-32B FP8 cache at 32768 tokens, bf16 predictor mean
         Workload("qwen3_32b_e4m3_32k", 5, 64, 8, 128, 32768, SYM_E4M3, MU_BF16, 0.04, 128, 512),
+        # Qwen3-32B geometry with an FP8-quantized copy of the cache as the predictor
+        Workload("qwen3_32b_bf16_fp8res", 6, 64, 8, 128, 8192, SYM_BF16, MU_BF16, 0.0, 128, 512, "fp8block"),
     ]
 }
 
@@ -125,6 +135,20 @@ def _residual(shape, g, device) -> torch.Tensor:
     return r
 
 
+FP8_BLOCK = 32  # channels per block-FP8 scale
+
+
+def fp8_block_roundtrip(xf: torch.Tensor) -> torch.Tensor:
+    """dequant(e4m3(x / scale)) * scale along the last dim in blocks of 32,
+    scale = amax(|x|) / 448 per block (fp32; an all-zero block keeps scale 1)."""
+    shp = xf.shape
+    xb = xf.reshape(*shp[:-1], shp[-1] // FP8_BLOCK, FP8_BLOCK)
+    amax = xb.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (xb / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).to(torch.float32)
+    return (q * scale).reshape(shp)
+
+
 def _slab(w: Workload, s_layer: torch.Tensor, tokens: int, seed: int, device):
     """One layer: x bits and mu for [2, H, tokens, D]."""
     g = _gen(seed, device)
@@ -132,7 +156,10 @@ def _slab(w: Workload, s_layer: torch.Tensor, tokens: int, seed: int, device):
     sc = s_layer.to(device).view(2, w.kv_heads, 1, w.head_dim)
     x16 = (sc * torch.randn(shape, generator=g, device=device)).to(torch.bfloat16)
     xf = x16.to(torch.float32)
-    mu = xf + (w.sigma_k * sc) * _residual(shape, g, device)
+    if w.mu_kind == "fp8block":
+        mu = fp8_block_roundtrip(xf)
+    else:
+        mu = xf + (w.sigma_k * sc) * _residual(shape, g, device)
     if w.sym_fmt == SYM_BF16:
         xb = x16.view(torch.int16)
     else:

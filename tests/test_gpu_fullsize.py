@@ -14,7 +14,7 @@ from gpu_util import DEV, ensure_built, np_mu, np_sym
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k"]
+NAMES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k", "qwen3_32b_bf16_fp8res"]
 CALIB_SEQS = 2  # the launch configuration does not depend on the calibration set's size
 
 

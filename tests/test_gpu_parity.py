@@ -25,7 +25,7 @@ def _reduced(name, layers=2, tokens=600, calib_seqs=2):
     return w, min(calib_seqs, w.calib_seqs)
 
 
-CASES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k"]
+CASES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k", "qwen3_32b_bf16_fp8res"]
 
 
 @pytest.mark.parametrize("name", CASES)
