@@ -139,9 +139,9 @@ __device__ __forceinline__ uint32_t guess_symbol(const ModelTabs &t, const float
                                                  float inv_step, float sinv, float m) {
   float mf = (tq - (float)a_guess<SYM, TAB>(t, k)) * inv_step;
   mf = __builtin_fminf(__builtin_fmaxf(mf, 0.0f), (float)kNInv - 0.5f);
-  const int ii = (int)mf;
+  const int ii = (int)mf;  // mf >= 0: truncation is the floor
   const float2 ud = uinv[ii];
-  const float uu = __builtin_fmaf(mf - (float)ii, ud.y, ud.x);
+  const float uu = __builtin_fmaf(__builtin_amdgcn_fractf(mf), ud.y, ud.x);
   const float e = __builtin_fmaf(uu, sinv, m);
   return SYM == SKV_SYM_BF16 ? bf16_rne_bits(e) : e4m3_guess(e);
 }
@@ -190,7 +190,9 @@ __device__ uint32_t search_rank(const ModelTabs &t, uint32_t k0, bool below, uin
   return lo;
 }
 
-// verify symbol g: d - r*cum_lo and whether it lies in [0, r*freq)
+// verify symbol g: d - r*cum_lo and whether it lies in [0, r*freq).  The
+// difference is taken modulo 2^64: when d < r*cum_lo it wraps above 2^63, far
+// beyond r*freq < 2^48, so one unsigned compare decides.  below: d < r*cum_lo.
 template <int SYM, int TAB>
 __device__ __forceinline__ bool verify(const ModelTabs &t, uint32_t g, float m, float s, uint64_t d, uint32_t r,
                                        int up, uint32_t &clo, uint32_t &chi, uint64_t &dd, uint64_t &pf,
@@ -198,12 +200,9 @@ __device__ __forceinline__ bool verify(const ModelTabs &t, uint32_t g, float m, 
   model_pair<SYM, TAB>(t, g, m, s, clo, chi);
   const uint64_t plo = mul24(r, clo << up);
   pf = mul24(r, (chi - clo) << up);
-  unsigned int b0, b1;
-  const uint32_t dl = __builtin_subc((uint32_t)d, (uint32_t)plo, 0u, &b0);
-  const uint32_t dh = __builtin_subc((uint32_t)(d >> 32), (uint32_t)(plo >> 32), b0, &b1);
-  dd = ((uint64_t)dh << 32) | dl;
-  below = b1 != 0;
-  return !below && dd < pf;
+  dd = d - plo;
+  below = d < plo;
+  return dd < pf;
 }
 
 // A lane's next kBatch predictor means (symbols i0, i0 + 64, ...), raw.
