@@ -283,6 +283,20 @@ template <int SYM, bool FAST>
 __device__ __forceinline__ void model_pair(const EncArgs &a, const EncTables &t, uint32_t b, float m, float sj,
                                            uint32_t &c, uint32_t &f) {
   if (SYM == SKV_SYM_BF16) {
+    // p_hat part first: it depends on b alone, so its table reads are in flight
+    // while the Gaussian pair is evaluated
+    const uint32_t k = rank_bf16(b);
+    uint32_t alo, ahi;
+    if (FAST) {
+      const uint32_t w = k >> 6;
+      const uint32_t e = k + w;  // = 65 w + (k mod 64)
+      const uint32_t base_w = t.ab[w];
+      alo = base_w + t.a16[e];
+      ahi = base_w + t.a16[e + 1];
+    } else {
+      alo = a.ptab[k];
+      ahi = a.ptab[k + 1];
+    }
     // The bin of a finite non-zero b is [(b-1):8000, b:8000] in fp32 bits for
     // b > 0 and the same pair swapped for b < 0; Cg is monotone, so the lower
     // count is the min of the two.  +-0, +-inf and NaN take the general edges.
@@ -299,18 +313,6 @@ __device__ __forceinline__ void model_pair(const EncArgs &a, const EncTables &t,
         glo = cg_eval(t.kn, u_of(lo, m, sj));
         ghi = cg_eval(t.kn, u_of(hi, m, sj));
       }
-    }
-    const uint32_t k = rank_bf16(b);
-    uint32_t alo, ahi;
-    if (FAST) {
-      const uint32_t w = k >> 6;
-      const uint32_t e = k + w;  // = 65 w + (k mod 64)
-      const uint32_t base_w = t.ab[w];
-      alo = base_w + t.a16[e];
-      ahi = base_w + t.a16[e + 1];
-    } else {
-      alo = a.ptab[k];
-      ahi = a.ptab[k + 1];
     }
     c = alo + glo;
     f = ahi + ghi - c;

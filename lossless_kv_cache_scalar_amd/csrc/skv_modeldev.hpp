@@ -77,6 +77,10 @@ template <int SYM, int TAB>
 __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float m, float s, uint32_t &clo,
                                            uint32_t &chi) {
   if (SYM == SKV_SYM_BF16) {
+    // p_hat part first: it depends on b alone, so its table reads are in flight
+    // while the Gaussian pair is evaluated
+    uint32_t alo, ahi;
+    a_pair<TAB>(t, rank_bf16(b), alo, ahi);
     // The bin of a finite non-zero b is [(b-1):8000, b:8000] in fp32 bits for
     // b > 0 and the same pair swapped for b < 0; Cg is monotone, so the lower
     // count is the min of the two.  +-0, +-inf and NaN take the general edges.
@@ -94,8 +98,6 @@ __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float
         ghi = cg_eval(t.kn, u_of(hi, m, s));
       }
     }
-    uint32_t alo, ahi;
-    a_pair<TAB>(t, rank_bf16(b), alo, ahi);
     clo = alo + glo;
     chi = ahi + ghi;
   } else {
