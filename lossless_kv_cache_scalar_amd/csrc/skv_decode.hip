@@ -64,8 +64,13 @@ struct LaneReader {
 
   __device__ __forceinline__ void issue() {
     const bool tl = w >= m;
-    uint32_t a0 = tl ? (tail + 4u * (w - m)) & ~3u : ip;
-    if (4u * w >= len) a0 = 0u;  // nothing left: any dword of the chunk, masked off below
+    uint32_t a0 = ip;  // an interleaved word never lies past the lane's end
+    if (__builtin_expect(__any(tl), 0)) {
+      if (tl) {
+        a0 = (tail + 4u * (w - m)) & ~3u;
+        if (4u * w >= len) a0 = 0u;  // nothing left: any dword of the chunk, masked off below
+      }
+    }
     plo = *reinterpret_cast<const uint32_t *>(chunk + a0);
     if (__builtin_expect(__any(tl), 0)) {
       uint32_t a1 = a0 + 4u;
@@ -73,6 +78,8 @@ struct LaneReader {
       phi = *reinterpret_cast<const uint32_t *>(chunk + a1);
     }
   }
+  // renormalisation bytes taken so far (after the 6 priming bytes)
+  __device__ __forceinline__ uint32_t renorm_bytes() const { return (32u * w - (uint32_t)nib) / 8u - 6u; }
   __device__ __forceinline__ uint32_t word() const {
     if (__builtin_expect(w < m, 1)) return __builtin_bswap32(plo);
     const uint32_t sh = 8u * (tail & 3u);
@@ -224,7 +231,7 @@ struct MuBatch {
 // Decode one symbol of a lane: returns its pattern and advances the coder.
 template <int SYM, int MU, int TAB>
 __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelTabs &t, const float2 *uinv,
-                                                  LaneReader &br, uint64_t &d, uint64_t &range, uint32_t &shifted,
+                                                  LaneReader &br, uint64_t &d, uint64_t &range,
                                                   bool &corrupt, float m, float sj, float sinvj) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   constexpr int up = BF ? 0 : 8;
@@ -274,7 +281,6 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & ~7u;  // pf >= r >= 2^16
   d = (dd << n8) | br.take(n8);
   range = pf << n8;
-  shifted += n8 >> 3;
   return gs;
 }
 
@@ -324,7 +330,6 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     uint64_t d = (uint64_t)br.take(24) << 24;
     d |= br.take(24);
     uint64_t range = kW48;
-    uint32_t shifted = 0;  // renormalisation bytes consumed
 
     // ---- symbols: lane l decodes scalars l, l + 64, ... of the chunk; symbol
     // k has channel (l + 64 k) mod D, which repeats with a period dividing kBatch
@@ -359,7 +364,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, cur.get(j), s[j],
+        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, cur.get(j), s[j],
                                                         sinv[j]);
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
@@ -381,13 +386,13 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       }
       const uint32_t mraw = cur.one(mu_ch, i);
       const float m = MU == SKV_MU_BF16 ? mu_from_bf16(mraw) : mu_from_f32(__uint_as_float(mraw));
-      const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, shifted, corrupt, m, sj, sij);
+      const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, m, sj, sij);
       br.issue();
       if (BF) static_cast<uint16_t *>(x_ch)[i] = (uint16_t)gs;
       else static_cast<uint8_t *>(x_ch)[i] = (uint8_t)gs;
     }
     // a substream of n renormalisations holds n + 1 bytes
-    if (shifted + 1 != len) corrupt = true;
+    if (br.renorm_bytes() + 1 != len) corrupt = true;
     if (corrupt) set_status(a.status, SKV_ERR_CORRUPT);
   }
 }
