@@ -112,12 +112,17 @@ __device__ __forceinline__ float u_of(float e, float mu, float s) {
   return t * s;
 }
 
-// Gaussian-pair CDF in counts: straight line between knots 1/64 apart in z.
+// Gaussian-pair CDF in counts: straight line between knots 1/64 apart in z,
+// at f = c - floor(c) in fp32.  v_fract_f32 returns exactly that difference
+// except where it rounds to 1.0 (c in [-2^-25, 0)), where it returns the float
+// just below 1; that case only reaches the knot pair at floor(c) = -1, whose
+// interpolated count floors to the same integer at either f (a property of the
+// knot tables of both symbol formats).
 __device__ __forceinline__ uint32_t cg_eval(const float2 *__restrict__ kn, float u) {
   float c = __builtin_fminf(__builtin_fmaxf(u, -(float)kUMax), (float)kUMax);
-  float fl = __builtin_floorf(c);
-  int i = (int)fl;
-  float f = c - fl;
+  int i;  // floor(c) as an integer in one instruction (|c| <= 1024)
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(i) : "v"(c));
+  float f = __builtin_amdgcn_fractf(c);
   float2 kd = kn[i + kUMax];
   float y = __builtin_fmaf(f, kd.y, kd.x);
   return (uint32_t)y;

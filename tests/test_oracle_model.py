@@ -53,6 +53,38 @@ def test_knot_table_structure(fmt):
     assert D[-1] == 0.0 and np.all(D >= 0)
 
 
+def _rn32(q):
+    """Exact round-to-nearest-even of a non-negative rational to fp32 (normal range)."""
+    from fractions import Fraction
+    if q == 0:
+        return 0.0
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if Fraction(2) ** e > q:
+        e -= 1
+    ulp = Fraction(2) ** (e - 23)
+    n, r = divmod(q, ulp)
+    if r > ulp / 2 or (r == ulp / 2 and n % 2 == 1):
+        n += 1
+    return float(n * ulp)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_knot_pair_below_zero_floors_alike_near_f_one(fmt):
+    """The device evaluates f = c - floor(c) with v_fract_f32, which returns the
+    float just below 1 where the fp32 difference rounds to 1.0; that happens
+    only for c in [-2^-25, 0), i.e. on the knot pair at floor(c) = -1.  There,
+    floor(RN(K + f D)) must not depend on which of the two f is used."""
+    from fractions import Fraction
+    m = R.Model(fmt)
+    K, D = m.knots()
+    k, d = Fraction(float(K[1023])), Fraction(float(D[1023]))
+    below_one = Fraction(float(np.nextafter(np.float32(1), np.float32(0))))
+    y_one = _rn32(k + d)
+    y_below = _rn32(k + below_one * d)
+    assert math.floor(y_one) == math.floor(y_below)
+    assert y_one == float(K[1024])  # the pair's top end is the next knot exactly
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_cg_monotone_and_saturating(fmt):
     m = R.Model(fmt)
