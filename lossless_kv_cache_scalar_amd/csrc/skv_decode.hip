@@ -284,7 +284,7 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   return gs;
 }
 
-template <int SYM, int MU, int TAB>
+template <int SYM, int MU, int PER, int TAB>
 __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs &t, const float2 *uinv) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   const Geo &g = a.g;
@@ -332,10 +332,11 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     uint64_t range = kW48;
 
     // ---- symbols: lane l decodes scalars l, l + 64, ... of the chunk; symbol
-    // k has channel (l + 64 k) mod D, which repeats with a period dividing kBatch
-    float s[kBatch], sinv[kBatch];
+    // k has channel (l + 64 k) mod D, which repeats with period PER = max(2, D / 64),
+    // a divisor of kBatch
+    float s[PER], sinv[PER];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
+    for (int j = 0; j < PER; ++j) {
       const float2 sc = a.scale[row * g.D + ((lane + kLanes * j) & (D - 1))];
       s[j] = sc.x;
       sinv[j] = sc.y;
@@ -343,7 +344,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     // wait for the scales here: a wait inside the symbol loop would also wait
     // for the loads in flight on every trip
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(s[j]), "v"(sinv[j]));
+    for (int j = 0; j < PER; ++j) asm volatile("" ::"v"(s[j]), "v"(sinv[j]));
     const void *mu_ch = MU == SKV_MU_BF16 ? (const void *)(static_cast<const uint16_t *>(a.mu) + base)
                                           : (const void *)(static_cast<const float *>(a.mu) + base);
     void *x_ch = BF ? (void *)(static_cast<uint16_t *>(a.x_out) + base) : (void *)(static_cast<uint8_t *>(a.x_out) + base);
@@ -364,8 +365,8 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, cur.get(j), s[j],
-                                                        sinv[j]);
+        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, cur.get(j),
+                                                        s[j % PER], sinv[j % PER]);
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
         else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
@@ -378,8 +379,8 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       const int j = k & (kBatch - 1);
       float sj = s[0], sij = sinv[0];
 #pragma unroll
-      for (int q = 1; q < kBatch; ++q) {
-        if (j == q) {
+      for (int q = 1; q < PER; ++q) {
+        if (j % PER == q) {
           sj = s[q];
           sij = sinv[q];
         }
@@ -397,7 +398,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
   }
 }
 
-template <int SYM, int MU>
+template <int SYM, int MU, int PER>
 __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   __shared__ float2 s_kn[kNKnot];
@@ -421,8 +422,8 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   }
   __syncthreads();
   const ModelTabs t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, a.ptab, s_et, 0u, kNWin};
-  if (!BF || win) decode_chunks<SYM, MU, kTabLdsAll>(a, t, s_ui);
-  else decode_chunks<SYM, MU, kTabGlobal>(a, t, s_ui);
+  if (!BF || win) decode_chunks<SYM, MU, PER, kTabLdsAll>(a, t, s_ui);
+  else decode_chunks<SYM, MU, PER, kTabGlobal>(a, t, s_ui);
 }
 
 static int dec_cu_count() {
@@ -441,7 +442,10 @@ static void launch_dec_kernel(const DecArgs &a, hipStream_t st) {
   const int64_t need = (a.g.n_chunks + kDecWaves - 1) / kDecWaves;
   const int64_t cus = dec_cu_count();
   const unsigned blocks = (unsigned)(need < cus ? need : cus);
-  hipLaunchKernelGGL((k_decode<SYM, MU>), dim3(blocks), dim3(kDecBlock), 0, st, a);
+  // the scale period of a lane's symbols: max(2, head_dim / 64)
+  if (a.g.D >= 512) hipLaunchKernelGGL((k_decode<SYM, MU, 8>), dim3(blocks), dim3(kDecBlock), 0, st, a);
+  else if (a.g.D >= 256) hipLaunchKernelGGL((k_decode<SYM, MU, 4>), dim3(blocks), dim3(kDecBlock), 0, st, a);
+  else hipLaunchKernelGGL((k_decode<SYM, MU, 2>), dim3(blocks), dim3(kDecBlock), 0, st, a);
 }
 
 hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes, const uint64_t *offsets,

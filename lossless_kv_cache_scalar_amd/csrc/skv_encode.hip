@@ -201,15 +201,14 @@ struct LaneCoder {
     offmax = 4u * ((cap_words - 1) * kLanes + lane);
   }
 
-  // Stores the word that starts at bit nbits - 32 of acc on every symbol, so
-  // every symbol issues the same memory operation (the waits for the batch
-  // loads stay exact); the store is final once those 32 bits are complete and
-  // is rewritten until then.  A valid model never fills the slot; a broken one
-  // rewrites its last word.
+  // Stores the word that starts at bit nbits - 32 of acc once those 32 bits
+  // are complete (a lane completes a word every few symbols, so most lanes of
+  // a store are masked off and the slot sees each word written once).  A
+  // valid model never fills the slot; a broken one rewrites its last word.
   __device__ __forceinline__ void flush_word() {
-    const uint32_t word = (uint32_t)(acc >> ((nbits - 32) & 63));
-    *reinterpret_cast<uint32_t *>(slot + off) = __builtin_bswap32(word);
     if (nbits >= 32) {
+      const uint32_t word = (uint32_t)(acc >> (nbits - 32));
+      *reinterpret_cast<uint32_t *>(slot + off) = __builtin_bswap32(word);
       ++nw;
       nbits -= 32;
       off = min(off + 4u * kLanes, offmax);
@@ -278,44 +277,43 @@ struct EncTables {
   const float2 *et;
 };
 
-// (c, f) of symbol b on the coder's 2^24 total
+// p_hat counts A(rank b), A(rank b + 1) of a bf16 symbol
+template <bool FAST>
+__device__ __forceinline__ void a_pair_bf16(const EncArgs &a, const EncTables &t, uint32_t b, uint32_t &alo,
+                                            uint32_t &ahi) {
+  const uint32_t k = rank_bf16(b);
+  if (FAST) {
+    const uint32_t w = k >> 6;
+    const uint32_t e = k + w;  // = 65 w + (k mod 64)
+    const uint32_t base_w = t.ab[w];
+    alo = base_w + t.a16[e];
+    ahi = base_w + t.a16[e + 1];
+  } else {
+    alo = a.ptab[k];
+    ahi = a.ptab[k + 1];
+  }
+}
+
+// (c, f) of symbol b on the coder's 2^24 total, for every b but the special
+// bf16 ones (+-0, +-inf, NaN), which report special = true and need
+// model_special.  The bin of a finite non-zero bf16 b is [(b-1):8000, b:8000]
+// in fp32 bits for b > 0 and the same pair swapped for b < 0; Cg is monotone,
+// so the lower count is the min of the two.
 template <int SYM, bool FAST>
-__device__ __forceinline__ void model_pair(const EncArgs &a, const EncTables &t, uint32_t b, float m, float sj,
-                                           uint32_t &c, uint32_t &f) {
+__device__ __forceinline__ void model_common(const EncArgs &a, const EncTables &t, uint32_t b, float m, float sj,
+                                             uint32_t &c, uint32_t &f, bool &special) {
   if (SYM == SKV_SYM_BF16) {
     // p_hat part first: it depends on b alone, so its table reads are in flight
     // while the Gaussian pair is evaluated
-    const uint32_t k = rank_bf16(b);
     uint32_t alo, ahi;
-    if (FAST) {
-      const uint32_t w = k >> 6;
-      const uint32_t e = k + w;  // = 65 w + (k mod 64)
-      const uint32_t base_w = t.ab[w];
-      alo = base_w + t.a16[e];
-      ahi = base_w + t.a16[e + 1];
-    } else {
-      alo = a.ptab[k];
-      ahi = a.ptab[k + 1];
-    }
-    // The bin of a finite non-zero b is [(b-1):8000, b:8000] in fp32 bits for
-    // b > 0 and the same pair swapped for b < 0; Cg is monotone, so the lower
-    // count is the min of the two.  +-0, +-inf and NaN take the general edges.
+    a_pair_bf16<FAST>(a, t, b, alo, ahi);
     const uint32_t eA = (b << 16) | 0x8000u;
     const uint32_t eB = eA - 0x10000u;
     const uint32_t cA = cg_eval(t.kn, u_of(__uint_as_float(eA), m, sj));
     const uint32_t cB = cg_eval(t.kn, u_of(__uint_as_float(eB), m, sj));
-    uint32_t glo = min(cA, cB), ghi = max(cA, cB);
-    const bool special = ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17);
-    if (__builtin_expect(__any(special), 0)) {
-      if (special) {
-        float lo, hi;
-        bf16_bin(b, lo, hi);
-        glo = cg_eval(t.kn, u_of(lo, m, sj));
-        ghi = cg_eval(t.kn, u_of(hi, m, sj));
-      }
-    }
-    c = alo + glo;
-    f = ahi + ghi - c;
+    special = ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17);
+    c = alo + min(cA, cB);
+    f = ahi + max(cA, cB) - c;
   } else {
     const float2 e = t.et[b];
     const uint32_t k = rank_e4m3(b);
@@ -323,10 +321,33 @@ __device__ __forceinline__ void model_pair(const EncArgs &a, const EncTables &t,
     const uint32_t hi = t.ab[k + 1] + cg_eval(t.kn, u_of(e.y, m, sj));
     c = lo << 8;
     f = (hi - lo) << 8;
+    special = false;
   }
 }
 
-template <int SYM, int MU, bool FAST>
+// (c, f) of a special bf16 symbol from its general bin edges
+template <bool FAST>
+__device__ __forceinline__ void model_special(const EncArgs &a, const EncTables &t, uint32_t b, float m, float sj,
+                                              uint32_t &c, uint32_t &f) {
+  uint32_t alo, ahi;
+  a_pair_bf16<FAST>(a, t, b, alo, ahi);
+  float lo, hi;
+  bf16_bin(b, lo, hi);
+  c = alo + cg_eval(t.kn, u_of(lo, m, sj));
+  f = ahi + cg_eval(t.kn, u_of(hi, m, sj)) - c;
+}
+
+template <int SYM, bool FAST>
+__device__ __forceinline__ void model_pair(const EncArgs &a, const EncTables &t, uint32_t b, float m, float sj,
+                                           uint32_t &c, uint32_t &f) {
+  bool special;
+  model_common<SYM, FAST>(a, t, b, m, sj, c, f, special);
+  if (SYM == SKV_SYM_BF16 && __builtin_expect(__any(special), 0)) {
+    if (special) model_special<FAST>(a, t, b, m, sj, c, f);
+  }
+}
+
+template <int SYM, int MU, int PER, bool FAST>
 __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables &t) {
   const Geo &g = a.g;
   const int lane = threadIdx.x & 63;
@@ -372,14 +393,14 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     const int64_t base = (row * g.tokens + blk * kChunkTokens) * g.D;
 
     // symbol k of the lane has channel (lane + 64 k) mod D; with D a power of
-    // two up to 512 that repeats with a period dividing kBatch
-    float s[kBatch];
+    // two up to 512 that repeats with period PER = max(2, D / 64), which divides kBatch
+    float s[PER];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) s[j] = a.scale[row * g.D + ((lane + kLanes * j) & (D - 1))].x;
+    for (int j = 0; j < PER; ++j) s[j] = a.scale[row * g.D + ((lane + kLanes * j) & (D - 1))].x;
     // wait for the scales here: a wait inside the symbol loop would also wait
     // for the batch loads in flight on every trip
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(s[j]));
+    for (int j = 0; j < PER; ++j) asm volatile("" ::"v"(s[j]));
 
     LaneCoder cod;
     cod.init(a.scratch + (uint64_t)chunk * kLanes * g.lane_cap, (uint32_t)lane, g.lane_cap / 4);
@@ -401,7 +422,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         uint32_t c, f;
-        model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), s[j], c, f);
+        model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), s[j % PER], c, f);
         cod.encode(c, f);
       }
       cur = nxt;
@@ -412,8 +433,8 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
       const int j = k & (kBatch - 1);
       float sj = s[0];
 #pragma unroll
-      for (int q = 1; q < kBatch; ++q)
-        if (j == q) sj = s[q];
+      for (int q = 1; q < PER; ++q)
+        if (j % PER == q) sj = s[q];
       cur.one(a, i, 0);
       uint32_t c, f;
       model_pair<SYM, FAST>(a, t, cur.xs[0], cur.mu(0), sj, c, f);
@@ -453,7 +474,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
   }
 }
 
-template <int SYM, int MU>
+template <int SYM, int MU, int PER>
 __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   __shared__ float2 s_kn[kNKnot];
@@ -475,8 +496,8 @@ __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   }
   __syncthreads();
   const EncTables t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, s_et};
-  if (fast) encode_chunks<SYM, MU, true>(a, t);
-  else encode_chunks<SYM, MU, false>(a, t);
+  if (fast) encode_chunks<SYM, MU, PER, true>(a, t);
+  else encode_chunks<SYM, MU, PER, false>(a, t);
 }
 
 __global__ void k_enc_reset(uint64_t *__restrict__ flags, int64_t n, uint32_t *__restrict__ ctr) {
@@ -501,7 +522,10 @@ static void launch_enc_kernel(const EncArgs &a, hipStream_t st) {
   const int64_t need = (a.g.n_chunks + kEncWaves - 1) / kEncWaves;
   const int64_t cus = cu_count();
   const unsigned blocks = (unsigned)(need < cus ? need : cus);
-  hipLaunchKernelGGL((k_encode<SYM, MU>), dim3(blocks), dim3(kEncBlock), 0, st, a);
+  // the scale period of a lane's symbols: max(2, head_dim / 64)
+  if (a.g.D >= 512) hipLaunchKernelGGL((k_encode<SYM, MU, 8>), dim3(blocks), dim3(kEncBlock), 0, st, a);
+  else if (a.g.D >= 256) hipLaunchKernelGGL((k_encode<SYM, MU, 4>), dim3(blocks), dim3(kEncBlock), 0, st, a);
+  else hipLaunchKernelGGL((k_encode<SYM, MU, 2>), dim3(blocks), dim3(kEncBlock), 0, st, a);
 }
 
 hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Workspace &ws, uint8_t *bits,
