@@ -185,8 +185,7 @@ struct LaneCoder {
   uint32_t nw, capw;
   uint32_t *out;   // the lane's word 0 in the chunk's slot
   uint8_t *slot;   // the chunk's slot (the same for the whole wave)
-  uint32_t off;    // byte offset of word min(nw, capw - 1) in the slot
-  uint32_t offmax;
+  uint32_t off;    // byte offset of the lane's word nw in the slot
 
   __device__ __forceinline__ void init(uint8_t *chunk_slot, uint32_t lane, uint32_t cap_words) {
     X = 0;
@@ -198,20 +197,19 @@ struct LaneCoder {
     slot = chunk_slot;
     out = reinterpret_cast<uint32_t *>(chunk_slot) + lane;
     off = 4u * lane;
-    offmax = 4u * ((cap_words - 1) * kLanes + lane);
   }
 
   // Stores the word that starts at bit nbits - 32 of acc once those 32 bits
   // are complete (a lane completes a word every few symbols, so most lanes of
-  // a store are masked off and the slot sees each word written once).  A
-  // valid model never fills the slot; a broken one rewrites its last word.
+  // a store are masked off and the slot sees each word written once).  At most
+  // 3 bytes per symbol plus the flush: the slot (lane_cap) always has room.
   __device__ __forceinline__ void flush_word() {
     if (nbits >= 32) {
       const uint32_t word = (uint32_t)(acc >> (nbits - 32));
       *reinterpret_cast<uint32_t *>(slot + off) = __builtin_bswap32(word);
       ++nw;
       nbits -= 32;
-      off = min(off + 4u * kLanes, offmax);
+      off += 4u * kLanes;
     }
   }
 
@@ -219,12 +217,19 @@ struct LaneCoder {
   __device__ __forceinline__ void encode(uint32_t c, uint32_t f) {
     const uint32_t r = (uint32_t)(range >> 24);  // range < 2^48
     __builtin_assume(r < (1u << 24));
-    const uint64_t p = mul24(r, c);
-    const uint64_t Xn = X + p;
-    const bool carry = Xn < p;  // out of bit 63
+    // the carry out of bit 63 compares the sum with the old X, which the empty
+    // asm hides from the optimiser (it would rewrite the test as Xn < r * c and
+    // form that product a second time)
+    uint64_t Xo = X;
+    asm("" : "+v"(Xo));
+    const uint64_t Xn = Xo + mul24(r, c);
+    const bool carry = Xn < Xo;
     X = Xn;
     const uint64_t rg = mul24(r, f);
-    const uint32_t n8 = __builtin_clz((uint32_t)(rg >> 16)) & ~7u;  // bytes to shift, x8
+    // bytes to shift, x8: rg >= 2^16 (f >= 1) makes this clz & ~7; the mask
+    // bounds it by 24 whatever rg is, so a lane never emits more than 3 bytes
+    // per symbol and never outgrows its slot
+    const uint32_t n8 = __builtin_clz((uint32_t)(rg >> 16)) & 24u;
     if (__builtin_expect(__any(carry), 0)) {
       if (carry) acc = carry_out(acc, nbits, out, nw, capw);
     }
