@@ -131,7 +131,7 @@ __device__ __forceinline__ uint32_t e4m3_guess(float e) {
   return sgn | min(code, 0x7Eu);
 }
 
-// A(k) for a guess
+// A(k) for a guess; k is the rank (e4m3) or the table index tix_bf16 (bf16)
 template <int SYM, int TAB>
 __device__ __forceinline__ uint32_t a_guess(const ModelTabs &t, uint32_t k) {
   if (SYM != SKV_SYM_BF16) return t.ab[k];
@@ -232,7 +232,7 @@ struct MuBatch {
 template <int SYM, int MU, int TAB>
 __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelTabs &t, const float2 *uinv,
                                                   LaneReader &br, uint64_t &d, uint64_t &range,
-                                                  bool &corrupt, float m, float sj, float sinvj) {
+                                                  bool &corrupt, float m, uint32_t mraw, float sj, float sinvj) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   constexpr int up = BF ? 0 : 8;
   constexpr uint32_t N = BF ? 65536u : 256u;
@@ -241,11 +241,12 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   // rank of mu, then with k the rank of that first guess (the one-count floor
   // makes A(k) grow by one per rank, which matters near zero)
   const float tq = (float)(uint32_t)(d >> 16) * (65536.0f * __builtin_amdgcn_rcpf((float)(r << up)));
+  // (any start serves: a non-finite bf16 mean starts from its own pattern)
   uint32_t kmu;
-  if (BF) kmu = rank_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : (__float_as_uint(m) >> 16));
+  if (BF) kmu = tix_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : mraw);
   else kmu = rank_e4m3(e4m3_guess(m));
   uint32_t gs = guess_symbol<SYM, TAB>(t, uinv, tq, kmu, a.inv_step, sinvj, m);
-  gs = guess_symbol<SYM, TAB>(t, uinv, tq, BF ? rank_bf16(gs) : rank_e4m3(gs), a.inv_step, sinvj, m);
+  gs = guess_symbol<SYM, TAB>(t, uinv, tq, BF ? tix_bf16(gs) : rank_e4m3(gs), a.inv_step, sinvj, m);
   // ---- verify exactly
   uint32_t clo, chi;
   uint64_t dd, pf;
@@ -365,7 +366,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, cur.get(j),
+        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, cur.get(j), cur.v[j],
                                                         s[j % PER], sinv[j % PER]);
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
@@ -387,7 +388,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       }
       const uint32_t mraw = cur.one(mu_ch, i);
       const float m = MU == SKV_MU_BF16 ? mu_from_bf16(mraw) : mu_from_f32(__uint_as_float(mraw));
-      const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, m, sj, sij);
+      const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, m, mraw, sj, sij);
       br.issue();
       if (BF) static_cast<uint16_t *>(x_ch)[i] = (uint16_t)gs;
       else static_cast<uint8_t *>(x_ch)[i] = (uint8_t)gs;
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
     for (int i = threadIdx.x; i < 256; i += kDecBlock) s_et[i] = a.etab[i];
   }
   __syncthreads();
-  const ModelTabs t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, a.ptab, s_et, 0u, kNWin};
+  const ModelTabs t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, a.ptab, s_et};
   if (!BF || win) decode_chunks<SYM, MU, PER, kTabLdsAll>(a, t, s_ui);
   else decode_chunks<SYM, MU, PER, kTabGlobal>(a, t, s_ui);
 }

@@ -286,14 +286,15 @@ struct EncTables {
 template <bool FAST>
 __device__ __forceinline__ void a_pair_bf16(const EncArgs &a, const EncTables &t, uint32_t b, uint32_t &alo,
                                             uint32_t &ahi) {
-  const uint32_t k = rank_bf16(b);
   if (FAST) {
-    const uint32_t w = k >> 6;
-    const uint32_t e = k + w;  // = 65 w + (k mod 64)
+    const uint32_t ti = tix_bf16(b);  // the window image's index of rank_bf16(b)
+    const uint32_t w = ti >> 6;
+    const uint32_t e = ti + w;  // = 65 w + (ti mod 64)
     const uint32_t base_w = t.ab[w];
     alo = base_w + t.a16[e];
     ahi = base_w + t.a16[e + 1];
   } else {
+    const uint32_t k = rank_bf16(b);
     alo = a.ptab[k];
     ahi = a.ptab[k + 1];
   }

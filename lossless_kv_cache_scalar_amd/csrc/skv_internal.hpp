@@ -73,6 +73,19 @@ struct Workspace {
 // ---- symbol order ----
 __device__ __forceinline__ uint32_t rank_bf16(uint32_t b) { return b ^ ((b & 0x8000u) ? 0xFFFFu : 0x8000u); }
 __device__ __forceinline__ uint32_t unrank_bf16(uint32_t k) { return k ^ ((k & 0x8000u) ? 0x8000u : 0xFFFFu); }
+// Index of bf16 pattern b in the device image of the p_hat window table:
+// rank_bf16(b) ^ 0x8000, that is b for b < 0x8000 and b ^ 0x7FFF above (two
+// instructions: a sign-bit extract and one bitwise op).  The image stores the
+// window of ranks [64 w, 64 w + 64) in slot w ^ (kNWin / 2), so consecutive
+// ranks of a window stay consecutive.
+__device__ __forceinline__ uint32_t tix_bf16(uint32_t b) {
+  // neg = all ones for b >= 0x8000 (bit 15 sign-extended), then b ^ (neg & 0x7FFF)
+  // as one three-input bitwise op (truth table 0x6c over (neg, b, 0x7FFF));
+  // written out because the compiler turns the plain C into compare + select + xor
+  uint32_t t;
+  asm("v_bfe_i32 %0, %1, 15, 1\n\tv_bitop3_b32 %0, %0, %1, %2 bitop3:0x6c" : "=&v"(t) : "v"(b), "s"(0x7FFFu));
+  return t;
+}
 __device__ __forceinline__ uint32_t rank_e4m3(uint32_t b) { return b ^ ((b & 0x80u) ? 0xFFu : 0x80u); }
 __device__ __forceinline__ uint32_t unrank_e4m3(uint32_t k) { return k ^ ((k & 0x80u) ? 0x80u : 0xFFu); }
 

@@ -61,7 +61,8 @@ __device__ __forceinline__ uint64_t floor_div(uint64_t num, uint64_t den) {
 // counts hist[unrank k] + 1 of each block, summed.  k_ptable: H(k) from the
 // block sums and a block scan, then A(k); for bf16 also the LDS image of the
 // table: window w's base A(64 w) and 65 u16 offsets A(64 w + j) - A(64 w),
-// j = 0..64, clearing aflag when some window's offsets do not fit 16 bits.
+// j = 0..64 (window w in slot w ^ 512), clearing aflag when some window's
+// offsets do not fit 16 bits.
 constexpr int kPtBlock = 1024;
 
 __device__ __forceinline__ uint64_t rank_count(const uint64_t *__restrict__ hist, uint32_t k, int bf16) {
@@ -128,19 +129,21 @@ __global__ __launch_bounds__(kPtBlock) void k_ptable(const uint64_t *__restrict_
   if (k == N - 1) A[N] = N + Mp;
   if (!bf16) return;
   // window image: thread j = 0 of a window holds its base; j = 63 also writes
-  // entry 64, A(64 w + 64) - A(64 w)
+  // entry 64, A(64 w + 64) - A(64 w).  Window w goes to slot w ^ (kNWin / 2),
+  // the order in which tix_bf16 indexes it.
   const uint32_t w = k / kWinRanks, j = k % kWinRanks;
+  const uint32_t ws = w ^ (uint32_t)(kNWin / 2);
   const uint32_t a0 = __shfl(ak, 0, 64);  // the window is this wave
-  if (j == 0) abase[w] = ak;
+  if (j == 0) abase[ws] = ak;
   uint32_t off = ak - a0;
   bool wide = off > 0xFFFFu;
-  a16[w * kWinEntries + j] = (uint16_t)off;
+  a16[ws * kWinEntries + j] = (uint16_t)off;
   if (j == kWinRanks - 1) {
     const uint32_t an = k + 1 + (uint32_t)floor_div((uint64_t)Mp * (H + c), total);
     const uint32_t on = an - a0;
     wide = wide || on > 0xFFFFu;
-    a16[w * kWinEntries + kWinRanks] = (uint16_t)on;
-    if (w == N / kWinRanks - 1) abase[w + 1] = an;
+    a16[ws * kWinEntries + kWinRanks] = (uint16_t)on;
+    if (w == N / kWinRanks - 1) abase[kNWin] = an;
   }
   if (__any(wide) && j == 0) atomicAnd(aflag, 0);
 }

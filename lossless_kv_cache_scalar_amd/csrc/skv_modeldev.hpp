@@ -17,59 +17,40 @@ __device__ __forceinline__ uint64_t mul24(uint32_t a, uint32_t b) {
   return (uint64_t)a * (uint64_t)b;
 }
 
-// Where the p_hat table A lives for a kernel.
+// Where the bf16 p_hat table A lives for a kernel.
 enum { kTabGlobal = 0,   // A from global memory only (the 16-bit window image does not fit)
-       kTabLdsAll = 1,   // all 1024 bf16 windows in LDS
-       kTabLdsWin = 2 }; // LDS holds windows [w0, w0 + nw); others from global memory
+       kTabLdsAll = 1 }; // all 1024 windows in LDS
 
 struct ModelTabs {
   const float2 *kn;      // LDS: knots (K_j, D_j)
-  const uint16_t *a16;   // LDS: window image, first window w0
-  const uint32_t *ab;    // LDS: window bases, first window w0 (e4m3: the full table A)
-  const uint32_t *ptab;  // global: full table A
+  const uint16_t *a16;   // LDS: window image (bf16), window slots as tix_bf16 orders them
+  const uint32_t *ab;    // LDS: window bases (bf16); e4m3: the full table A in rank order
+  const uint32_t *ptab;  // global: full table A in rank order
   const float2 *et;      // LDS: e4m3 bins
-  uint32_t w0, nw;
 };
 
+// A(k) and A(k + 1) of bf16 rank k, given as its table index ti = k ^ 0x8000
 template <int TAB>
-__device__ __forceinline__ void a_pair(const ModelTabs &t, uint32_t k, uint32_t &alo, uint32_t &ahi) {
+__device__ __forceinline__ void a_pair(const ModelTabs &t, uint32_t ti, uint32_t &alo, uint32_t &ahi) {
   if (TAB == kTabGlobal) {
+    const uint32_t k = ti ^ 0x8000u;
     alo = t.ptab[k];
     ahi = t.ptab[k + 1];
     return;
   }
-  const uint32_t w = k >> 6;
-  if (TAB == kTabLdsAll) {
-    const uint32_t e = k + w;  // = 65 w + (k mod 64)
-    const uint32_t base = t.ab[w];
-    alo = base + t.a16[e];
-    ahi = base + t.a16[e + 1];
-    return;
-  }
-  const uint32_t wl = w - t.w0;
-  const bool out = wl >= t.nw;
-  const uint32_t wc = out ? 0u : wl;
-  const uint32_t e = 65u * wc + (k & 63u);
-  const uint32_t base = t.ab[wc];
+  const uint32_t w = ti >> 6;
+  const uint32_t e = ti + w;  // = 65 w + (ti mod 64)
+  const uint32_t base = t.ab[w];
   alo = base + t.a16[e];
   ahi = base + t.a16[e + 1];
-  if (__builtin_expect(__any(out), 0)) {
-    if (out) {
-      alo = t.ptab[k];
-      ahi = t.ptab[k + 1];
-    }
-  }
 }
 
-// A(k) alone (k <= N)
+// A(k) alone of bf16 rank k < N, given as its table index ti = k ^ 0x8000
 template <int TAB>
-__device__ __forceinline__ uint32_t a_one(const ModelTabs &t, uint32_t k) {
-  if (TAB == kTabGlobal) return t.ptab[k];
-  const uint32_t w = k >> 6;
-  if (TAB == kTabLdsAll) return t.ab[w] + t.a16[k + w];
-  const uint32_t wl = w - t.w0;
-  if (wl >= t.nw) return t.ptab[k];
-  return t.ab[wl] + t.a16[65u * wl + (k & 63u)];
+__device__ __forceinline__ uint32_t a_one(const ModelTabs &t, uint32_t ti) {
+  if (TAB == kTabGlobal) return t.ptab[ti ^ 0x8000u];
+  const uint32_t w = ti >> 6;
+  return t.ab[w] + t.a16[ti + w];
 }
 
 // cum_lo and cum_hi of symbol b in model units (bf16: total 2^24, e4m3: 2^16)
@@ -80,7 +61,7 @@ __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float
     // p_hat part first: it depends on b alone, so its table reads are in flight
     // while the Gaussian pair is evaluated
     uint32_t alo, ahi;
-    a_pair<TAB>(t, rank_bf16(b), alo, ahi);
+    a_pair<TAB>(t, tix_bf16(b), alo, ahi);
     // The bin of a finite non-zero b is [(b-1):8000, b:8000] in fp32 bits for
     // b > 0 and the same pair swapped for b < 0; Cg is monotone, so the lower
     // count is the min of the two.  +-0, +-inf and NaN take the general edges.
@@ -121,7 +102,7 @@ __device__ __forceinline__ uint32_t cum_rank(const ModelTabs &t, uint32_t k, flo
     if (__builtin_expect(__any(special), 0)) {
       if (special) e = __float_as_uint(bf16_lo_edge(b));
     }
-    return a_one<TAB>(t, k) + cg_eval(t.kn, u_of(__uint_as_float(e), m, s));
+    return a_one<TAB>(t, k ^ 0x8000u) + cg_eval(t.kn, u_of(__uint_as_float(e), m, s));
   } else {
     if (k >= 256u) return 1u << 16;
     return t.ab[k] + cg_eval(t.kn, u_of(t.et[unrank_e4m3(k)].x, m, s));
