@@ -11,10 +11,11 @@
 // r * cum_lo(s) <= d < r * cum_hi(s).  A guess comes from inverting the
 // Gaussian pair's CDF at t ~ d / r (fp32, approximate on purpose), twice: at
 // t - A(rank of mu), then at t - A(rank of the first guess).  The guess is
-// verified with the exact integer model and exact 48-bit products.  A miss
-// takes one secant step in rank space from the guess's exact counts, then, if
-// needed, a galloping search over ranks.  Any exact search returns the same
-// symbol, so the output does not depend on the guesses.
+// verified with the exact integer model and exact 48-bit products.  The rare
+// lanes whose guess misses are then resolved one at a time by the whole wave,
+// 64 probes of the exact cumulative count per round (a call with idle lanes,
+// in a short chunk's last batch, searches lane by lane instead).  Any exact
+// search returns the same symbol, so the output does not depend on the guesses.
 //
 // Stream reads.  Word w of a lane is word 64 w + l of the chunk's interleaved
 // region while w < m, so the lanes' refills read 256 contiguous bytes; each
@@ -228,6 +229,118 @@ struct MuBatch {
   }
 };
 
+// A lane whose guess missed, on its own (for the rare calls where not every
+// lane of the wave is active): one secant step in rank space from the guess's
+// exact counts, then galloping and bisection.
+template <int SYM, int TAB>
+__device__ __forceinline__ void resolve_alone(const ModelTabs &t, bool ok, bool below, float tq, uint32_t &gs,
+                                              uint32_t &clo, uint32_t &chi, float m, float sj, uint64_t d, uint32_t r,
+                                              uint64_t &dd, uint64_t &pf, bool &corrupt) {
+  constexpr bool BF = SYM == SKV_SYM_BF16;
+  constexpr int up = BF ? 0 : 8;
+  constexpr uint32_t N = BF ? 65536u : 256u;
+  if (!ok) {
+    // one secant step in rank space on the guess's exact counts
+    const uint32_t kg = BF ? rank_bf16(gs) : rank_e4m3(gs);
+    const float st = (tq - (float)clo) * __builtin_amdgcn_rcpf((float)(chi - clo));
+    int step = (int)__builtin_floorf(__builtin_fminf(__builtin_fmaxf(st, -70000.0f), 70000.0f));
+    step = below ? min(step, -1) : max(step, 1);
+    const int k2 = min(max((int)kg + step, 0), (int)N - 1);
+    uint32_t lo = below ? 0u : kg + 1, hi = below ? kg : N;  // holds at lo, fails at hi
+    if (lo < hi && (uint32_t)k2 >= lo && (uint32_t)k2 < hi) {
+      gs = BF ? unrank_bf16((uint32_t)k2) : unrank_e4m3((uint32_t)k2);
+      bool below2;
+      if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
+        const uint32_t ks = search_rank<SYM, TAB>(t, (uint32_t)k2, below2, lo, hi, d, r, up, m, sj);
+        gs = BF ? unrank_bf16(ks) : unrank_e4m3(ks);
+        if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
+          corrupt = true;  // no symbol holds d
+          dd = 0;
+        }
+      }
+    } else {
+      corrupt = true;  // d beyond the last symbol
+      dd = 0;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// The lanes whose guess missed, one at a time, with the whole wave (every lane
+// must be active): lane L's answer is the largest rank k with r * cum(k) <= d,
+// and the wave evaluates cum at 64 ranks per round.  The first round takes the 64 ranks next to the
+// guess on the side the verify pointed to (about 94% of misses end there);
+// later rounds spread 64 probes over the remaining bracket [lo, hi), so a
+// bracket of 65,536 ranks needs three more rounds at most.  cum(lo) <= t <
+// cum(hi) holds throughout (cum(0) = 0, cum(N) = T), and the counts at both
+// ends are kept, so the answer's pair comes with the last round.
+template <int SYM, int TAB>
+__device__ __forceinline__ void resolve_misses(const ModelTabs &t, bool miss, bool below, uint32_t &gs, uint32_t &clo,
+                                            uint32_t &chi, float m, float s, uint64_t d, uint32_t r, uint64_t &dd,
+                                            uint64_t &pf, bool &corrupt) {
+  constexpr bool BF = SYM == SKV_SYM_BF16;
+  constexpr int up = BF ? 0 : 8;
+  constexpr uint32_t N = BF ? 65536u : 256u;
+  constexpr uint32_t T = BF ? (1u << 24) : (1u << 16);
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t kg = BF ? rank_bf16(gs) : rank_e4m3(gs);
+  uint64_t pend = __ballot(miss);
+  while (pend) {
+    const int L = __builtin_ctzll(pend);
+    pend &= pend - 1;
+    const float mL = __uint_as_float(lane_u32(__float_as_uint(m), L));
+    const float sL = __uint_as_float(lane_u32(__float_as_uint(s), L));
+    const uint64_t dL = ((uint64_t)lane_u32((uint32_t)(d >> 32), L) << 32) | lane_u32((uint32_t)d, L);
+    const uint32_t rL = lane_u32(r, L);
+    const uint32_t kgL = lane_u32(kg, L);
+    uint32_t lo, hi, clo_b, chi_b, start;
+    if ((__ballot(below) >> L) & 1) {
+      lo = 0, clo_b = 0, hi = kgL, chi_b = lane_u32(clo, L);
+      start = hi > 64u ? hi - 64u : 0u;
+    } else {
+      lo = kgL + 1u, clo_b = lane_u32(chi, L), hi = N, chi_b = T;
+      start = lo;
+    }
+    for (int round = 0; hi - lo > 1u && round < 8; ++round) {
+      uint32_t kj;
+      if (hi - lo <= 64u) kj = lo + lane;
+      else if (round == 0) kj = start + lane;
+      else kj = lo + (uint32_t)(((uint64_t)(hi - lo) * lane) >> 6);
+      const bool valid = kj < hi;
+      const uint32_t cj = cum_rank<SYM, TAB>(t, valid ? kj : lo, mL, sL);
+      const uint64_t bal = __ballot(valid && mul24(rL, cj << up) <= dL);
+      if (bal == 0) {  // even the first probe lies above the answer
+        hi = lane_u32(kj, 0);
+        chi_b = lane_u32(cj, 0);
+        continue;
+      }
+      const int js = 63 - __builtin_clzll(bal);
+      lo = lane_u32(kj, js);
+      clo_b = lane_u32(cj, js);
+      if (js < 63 && ((__ballot(valid) >> (js + 1)) & 1)) {
+        hi = lane_u32(kj, js + 1);
+        chi_b = lane_u32(cj, js + 1);
+      }
+    }
+    if (lane == (uint32_t)L) {
+      gs = BF ? unrank_bf16(lo) : unrank_e4m3(lo);
+      clo = clo_b;
+      chi = chi_b;
+      const uint64_t plo = mul24(r, clo << up);
+      pf = mul24(r, (chi - clo) << up);
+      dd = d - plo;
+      if (hi - lo != 1u || d < plo || dd >= pf) {  // no symbol holds d
+        corrupt = true;
+        dd = 0;
+        pf = (uint64_t)r << 16;  // keeps the renormalisation within 3 bytes
+      }
+    }
+  }
+}
+
 // Decode one symbol of a lane: returns its pattern and advances the coder.
 template <int SYM, int MU, int TAB>
 __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelTabs &t, const float2 *uinv,
@@ -253,33 +366,11 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   bool below;
   const bool ok = verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below);
   if (__builtin_expect(__any(!ok), 0)) {
-    if (!ok) {
-      // one secant step in rank space on the guess's exact counts
-      const uint32_t kg = BF ? rank_bf16(gs) : rank_e4m3(gs);
-      const float st = (tq - (float)clo) * __builtin_amdgcn_rcpf((float)(chi - clo));
-      int step = (int)__builtin_floorf(__builtin_fminf(__builtin_fmaxf(st, -70000.0f), 70000.0f));
-      step = below ? min(step, -1) : max(step, 1);
-      const int k2 = min(max((int)kg + step, 0), (int)N - 1);
-      uint32_t lo = below ? 0u : kg + 1, hi = below ? kg : N;  // holds at lo, fails at hi
-      if (lo < hi && (uint32_t)k2 >= lo && (uint32_t)k2 < hi) {
-        gs = BF ? unrank_bf16((uint32_t)k2) : unrank_e4m3((uint32_t)k2);
-        bool below2;
-        if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
-          const uint32_t ks = search_rank<SYM, TAB>(t, (uint32_t)k2, below2, lo, hi, d, r, up, m, sj);
-          gs = BF ? unrank_bf16(ks) : unrank_e4m3(ks);
-          if (!verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below2)) {
-            corrupt = true;  // no symbol holds d
-            dd = 0;
-          }
-        }
-      } else {
-        corrupt = true;  // d beyond the last symbol
-        dd = 0;
-      }
-    }
+    if (__ballot(1) == ~0ull) resolve_misses<SYM, TAB>(t, !ok, below, gs, clo, chi, m, sj, d, r, dd, pf, corrupt);
+    else resolve_alone<SYM, TAB>(t, ok, below, tq, gs, clo, chi, m, sj, d, r, dd, pf, corrupt);
   }
   // ---- update and renormalise
-  const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & ~7u;  // pf >= r >= 2^16
+  const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & 24u;  // pf >= r >= 2^16: clz & ~7
   d = (dd << n8) | br.take(n8);
   range = pf << n8;
   return gs;

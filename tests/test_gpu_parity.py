@@ -161,6 +161,41 @@ def test_corrupt_stream_is_reported():
     assert int(buf.status.item()) == skv.ERR_CORRUPT
 
 
+@pytest.mark.parametrize("name", ["tiny_bf16", "qwen3_0.6b_e4m3"])
+def test_corrupt_payload_status_matches_oracle(name):
+    """Garbage inside a chunk's coded words (headers intact) drives the
+    decoder's search into and past the alphabet's ends; the GPU must finish,
+    and report corruption exactly when the oracle does."""
+    w, ns = _reduced(name, layers=1, tokens=300)
+    seqs = [synth.calibration_set(w, j) for j in range(ns)]
+    rsigma, rhist = oracle_calibrate(w, seqs)
+    x, mu = synth.generate(w)
+    sh, rsh = shapes(w)
+    sigma = torch.from_numpy(rsigma).to(DEV)
+    hist = torch.from_numpy(rhist.view(np.int64)).to(DEV)
+    bits, offs, out, st_e, st_d = gpu_roundtrip(sh, x.to(DEV), mu.to(DEV), sigma, hist)
+    assert st_e == skv.OK and st_d == skv.OK
+    m = R.Model(w.sym_fmt, rhist)
+    mn = np_mu(mu, w.mu_fmt)
+    rng = np.random.default_rng(7)
+    for trial in range(4):
+        bad = bits.copy()
+        c = int(rng.integers(0, len(offs) - 1))
+        lo, hi = int(offs[c]) + 128, int(offs[c + 1])  # past the chunk's length header
+        pos = rng.integers(lo, hi, size=24)
+        bad[pos] ^= rng.integers(1, 256, size=24).astype(np.uint8)
+        buf = skv.Buffers(sh, device=DEV)
+        dev_bits = torch.from_numpy(bad).to(DEV)
+        got = torch.empty_like(x, device=DEV)
+        buf.decode(mu.to(DEV), sigma, hist, got, bits=dev_bits, offsets=torch.from_numpy(offs.view(np.int64)).to(DEV))
+        torch.cuda.synchronize()
+        st_gpu = int(buf.status.item())
+        rout, st_ref = m.decode(rsh, bad, offs, mn, rsigma)
+        assert st_gpu == st_ref, (trial, c, st_gpu, st_ref)
+        if st_ref == R.OK:
+            assert np.array_equal(np_sym(got.cpu(), w.sym_fmt), rout)
+
+
 def test_bad_sigma_is_reported():
     w, sh, x, mu, sigma, hist = _tiny_inputs()
     buf = skv.Buffers(sh, device=DEV)
