@@ -117,10 +117,31 @@ struct LaneReader {
     nib -= (int)n;
     return v;
   }
+  // (x << n) | take(n) for x < 2^(64 - n), as two 64-bit shifts: the high
+  // word of x << n, and the high word of (low word of x : next bits) << n
+  __device__ __forceinline__ uint64_t shift_in(uint64_t x, uint32_t n) {
+    if (nib < (int)n) {  // nib <= 23
+      ib |= (uint64_t)word() << (32 - nib);
+      nib += 32;
+      ++w;
+      ip += 4u * kLanes;
+    }
+    const uint64_t lo = (((uint64_t)(uint32_t)x << 32) | (uint32_t)(ib >> 32)) << n;
+    const uint64_t r = ((x << n) & 0xFFFFFFFF00000000ull) | (lo >> 32);
+    ib <<= n;
+    nib -= (int)n;
+    return r;
+  }
 };
 
-// bf16 pattern of x, rounded to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+// bf16 pattern of x, rounded to nearest even, in the low half of a zero word:
+// v_cvt_pk_bf16_f32 with 0.0 as the second operand (written out so that the
+// compiler knows the high half is zero and masks nothing)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  uint32_t v;
+  asm("v_cvt_pk_bf16_f32 %0, %1, 0" : "=v"(v) : "v"(x));
+  return v;
+}
 
 // e4m3 pattern near e (round to nearest, saturating): a first guess only
 __device__ __forceinline__ uint32_t e4m3_guess(float e) {
@@ -371,7 +392,7 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   }
   // ---- update and renormalise
   const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & 24u;  // pf >= r >= 2^16: clz & ~7
-  d = (dd << n8) | br.take(n8);
+  d = br.shift_in(dd, n8);
   range = pf << n8;
   return gs;
 }
@@ -413,7 +434,9 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       continue;
     }
     LaneReader br;
-    br.chunk = a.bits + o0;
+    // the chunk's start is the same for the whole wave: in SGPRs, so the
+    // lanes' stream reads take a scalar base and a 32-bit lane offset
+    br.chunk = a.bits + (((uint64_t)lane_u32((uint32_t)(o0 >> 32), 0) << 32) | lane_u32((uint32_t)o0, 0));
     br.csize = (uint32_t)nbytes;
     br.m = mw;
     br.tail = kHeaderBytes + 4u * kLanes * mw + inc - (len - 4u * mw);

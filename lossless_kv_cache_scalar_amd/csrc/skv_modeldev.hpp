@@ -64,23 +64,25 @@ __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float
     a_pair<TAB>(t, tix_bf16(b), alo, ahi);
     // The bin of a finite non-zero b is [(b-1):8000, b:8000] in fp32 bits for
     // b > 0 and the same pair swapped for b < 0; Cg is monotone, so the lower
-    // count is the min of the two.  +-0, +-inf and NaN take the general edges.
+    // count is the min of the two.  +-0, +-inf and NaN take the general edges
+    // (the counts are complete before that rare branch, which redoes them, so
+    // the table reads and their sums stay in one block).
     const uint32_t eA = (b << 16) | 0x8000u;
     const uint32_t eB = eA - 0x10000u;
     const uint32_t cA = cg_eval(t.kn, u_of(__uint_as_float(eA), m, s));
     const uint32_t cB = cg_eval(t.kn, u_of(__uint_as_float(eB), m, s));
-    uint32_t glo = min(cA, cB), ghi = max(cA, cB);
+    clo = alo + min(cA, cB);
+    chi = ahi + max(cA, cB);
     const bool special = ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17);
     if (__builtin_expect(__any(special), 0)) {
       if (special) {
+        a_pair<TAB>(t, tix_bf16(b), alo, ahi);
         float lo, hi;
         bf16_bin(b, lo, hi);
-        glo = cg_eval(t.kn, u_of(lo, m, s));
-        ghi = cg_eval(t.kn, u_of(hi, m, s));
+        clo = alo + cg_eval(t.kn, u_of(lo, m, s));
+        chi = ahi + cg_eval(t.kn, u_of(hi, m, s));
       }
     }
-    clo = alo + glo;
-    chi = ahi + ghi;
   } else {
     const float2 e = t.et[b];
     const uint32_t k = rank_e4m3(b);
