@@ -48,9 +48,12 @@ enum { REF_OK = 0, REF_ERR_ARG = 1, REF_ERR_UNSUPPORTED = 2,
 enum { REF_SYM_BF16 = 0, REF_SYM_E4M3 = 1 };
 enum { REF_MU_BF16 = 0, REF_MU_F32 = 1 };
 
+enum { REF_SIGMA_CHANNEL = 0, REF_SIGMA_OCTAVE = 1 };
+
 typedef struct {
   int64_t layers, kv_heads, tokens, head_dim;
   int32_t sym_fmt, mu_fmt;
+  int32_t sigma_mode, reserved;
 } ref_shape;
 
 /* ---- model geometry ---- */
@@ -166,6 +169,32 @@ float skvref_scale(float sigma) {
 }
 
 static float mu_prime(float mu) { return isfinite(mu) ? mu : 0.0f; }
+
+/*
+ * sigma conditioned on the predictor's magnitude (SKV_SIGMA_OCTAVE).  The
+ * pages name a static per-channel sigma as a cost, the residual's size
+ * varying with position and prompt ([SKV] "下一步计划"); here sigma also
+ * depends on |mu'|, a quantity both ends know.  Reading: the octave of a scalar
+ * is j = clamp(E(mu') - E(sigma'_c) - 1, 0, 7), E the fp32 biased exponent
+ * field (0 for zero and subnormals), sigma'_c = max(sigma_c, 2^-100) the
+ * channel's own sigma; sigma is then looked up per (channel, octave).  Table
+ * layout per channel: OCT_STRIDE floats, [0] = sigma_c, [1 + j] = sigma_c,j.
+ */
+#define OCTAVES 8
+#define OCT_STRIDE (1 + OCTAVES)
+#define OCT_MIN_COUNT 16
+
+static uint32_t exp_field(float v) {
+  uint32_t u;
+  memcpy(&u, &v, 4);
+  return (u >> 23) & 0xFFu;
+}
+
+static int octave_of(float mp, float sigma_c) {
+  float sg = sigma_c > 0x1p-100f ? sigma_c : 0x1p-100f;
+  int j = (int)exp_field(mp) - (int)exp_field(sg) - 1;
+  return j < 0 ? 0 : (j > OCTAVES - 1 ? OCTAVES - 1 : j);
+}
 
 static float u_of(float e, float mu, float s) {
   float t = e - mu;
@@ -432,6 +461,7 @@ static int shape_ok(const ref_shape *sh) {
   if (sh->layers < 1 || sh->kv_heads < 1 || sh->tokens < 1 || sh->head_dim < 1) return REF_ERR_ARG;
   if (sh->sym_fmt != REF_SYM_BF16 && sh->sym_fmt != REF_SYM_E4M3) return REF_ERR_ARG;
   if (sh->mu_fmt != REF_MU_BF16 && sh->mu_fmt != REF_MU_F32) return REF_ERR_ARG;
+  if (sh->sigma_mode != REF_SIGMA_CHANNEL && sh->sigma_mode != REF_SIGMA_OCTAVE) return REF_ERR_ARG;
   /* head_dim a power of two from 8 to 512 (a multiple of 8 dividing 512) */
   if (sh->head_dim % 8 != 0 || 512 % sh->head_dim != 0) return REF_ERR_UNSUPPORTED;
   return REF_OK;
@@ -495,9 +525,39 @@ static uint64_t lane_byte_pos(const uint64_t *lens, uint64_t m, int l, uint64_t 
   return p + (j - 4 * m);
 }
 
+/* sigma floats per channel in the caller's sigma array */
+static int64_t sigma_stride(const ref_shape *sh) {
+  return sh->sigma_mode == REF_SIGMA_OCTAVE ? OCT_STRIDE : 1;
+}
+
+/* Per-channel scales of a row: s[d * OCTAVES + j] (channel mode: the same s
+   for every j) and the channel sigmas that fix the octave grid. */
+typedef struct {
+  float s[512 * OCTAVES];
+  float sig[512];
+  int octave;
+} row_scales;
+
+static void row_scales_init(row_scales *rs, const ref_shape *sh, const float *sigma_row) {
+  int64_t D = sh->head_dim;
+  rs->octave = sh->sigma_mode == REF_SIGMA_OCTAVE;
+  for (int64_t d = 0; d < D; d++) {
+    for (int j = 0; j < OCTAVES; j++)
+      rs->s[d * OCTAVES + j] = skvref_scale(rs->octave ? sigma_row[d * OCT_STRIDE + 1 + j] : sigma_row[d]);
+    rs->sig[d] = rs->octave ? sigma_row[d * OCT_STRIDE] : sigma_row[d];
+  }
+}
+
+/* the scale of a scalar of channel d whose mean is mu (raw) */
+static float scale_at(const row_scales *rs, int64_t d, float mu) {
+  int j = rs->octave ? octave_of(mu_prime(mu), rs->sig[d]) : 0;
+  return rs->s[d * OCTAVES + j];
+}
+
 /*
  * Encode one chunk.  x_c / mu_c point at the chunk's first scalar,
- * sigma_row at the row's head_dim sigmas.  Writes at most cap bytes to out;
+ * sigma_row at the row's sigmas (head_dim of them, or head_dim tables of
+ * OCT_STRIDE in octave mode).  Writes at most cap bytes to out;
  * returns the chunk's byte size (which may exceed cap: then *status is
  * REF_ERR_CAPACITY and out holds a prefix).
  */
@@ -507,8 +567,8 @@ uint64_t skvref_encode_chunk(const ref_model *m, const ref_shape *sh, int64_t ch
   chunk_geo g = geometry(sh, chunk);
   int64_t D = sh->head_dim;
   uint32_t up = 24u - m->log2T;  /* scale to the coder's 2^24 total */
-  float s[512];
-  for (int64_t d = 0; d < D; d++) s[d] = skvref_scale(sigma_row[d]);
+  row_scales *rs = (row_scales *)malloc(sizeof(row_scales));
+  row_scales_init(rs, sh, sigma_row);
   size_t lane_cap = (size_t)(3 * 4 * D + 8);
   uint8_t *lane_buf = (uint8_t *)malloc(lane_cap * LANES);
   uint64_t lens[LANES];
@@ -519,12 +579,13 @@ uint64_t skvref_encode_chunk(const ref_model *m, const ref_shape *sh, int64_t ch
       uint32_t b = sym_at(sh->sym_fmt, x_c, i);
       float mu = mu_at(sh->mu_fmt, mu_c, i);
       uint32_t clo, chi;
-      skvref_cum_pair(m, mu, s[i % D], b, &clo, &chi);
+      skvref_cum_pair(m, mu, scale_at(rs, i % D, mu), b, &clo, &chi);
       rc_encode(&e, (uint64_t)clo << up, (uint64_t)(chi - clo) << up);
     }
     rc_finish(&e);
     lens[lane] = e.n;
   }
+  free(rs);
   uint64_t total = HEADER_BYTES;
   for (int l = 0; l < LANES; l++) total += lens[l];
   uint64_t size = (total + 3) & ~3ull;
@@ -561,9 +622,9 @@ int skvref_decode_chunk(const ref_model *m, const ref_shape *sh, int64_t chunk,
   int64_t D = sh->head_dim;
   uint32_t up = 24u - m->log2T;
   int st = REF_OK;
-  float s[512];
-  for (int64_t d = 0; d < D; d++) s[d] = skvref_scale(sigma_row[d]);
   if (nbytes < HEADER_BYTES) return REF_ERR_CORRUPT;
+  row_scales *rs = (row_scales *)malloc(sizeof(row_scales));
+  row_scales_init(rs, sh, sigma_row);
   uint64_t lens[LANES], total = HEADER_BYTES;
   for (int l = 0; l < LANES; l++) {
     lens[l] = (uint64_t)bytes[2 * l] | ((uint64_t)bytes[2 * l + 1] << 8);
@@ -582,8 +643,9 @@ int skvref_decode_chunk(const ref_model *m, const ref_shape *sh, int64_t chunk,
     rc_dec_init(&q, lane, (size_t)lens[l]);
     uint64_t shifts = 0;
     for (int64_t i = l; i < g.nsc; i += LANES) {
-      float mp = mu_prime(mu_at(sh->mu_fmt, mu_c, i));
-      float sc = s[i % D];
+      float mu = mu_at(sh->mu_fmt, mu_c, i);
+      float mp = mu_prime(mu);
+      float sc = scale_at(rs, i % D, mu);
       uint64_t r = q.range >> 24;
       uint64_t t = q.d / (r << up);
       if (t >= m->T) { st = REF_ERR_CORRUPT; t = m->T - 1; }
@@ -609,6 +671,7 @@ int skvref_decode_chunk(const ref_model *m, const ref_shape *sh, int64_t chunk,
     if (lens[l] == 0 || shifts + 1 != lens[l]) st = REF_ERR_CORRUPT;
   }
   free(lane);
+  free(rs);
   return st;
 }
 
@@ -642,7 +705,7 @@ static void *enc_worker(void *p) {
     uint64_t n = skvref_encode_chunk(w->m, w->sh, c,
                                      (const uint8_t *)w->x + g.base * sym_bytes(w->sh),
                                      (const uint8_t *)w->mu + g.base * mu_bytes(w->sh),
-                                     w->sigma + g.row * w->sh->head_dim,
+                                     w->sigma + g.row * w->sh->head_dim * sigma_stride(w->sh),
                                      w->buf + used, w->buf_cap - used, &st);
     if (st != REF_OK) { w->status = st; return NULL; }
     w->sizes[c] = n;
@@ -659,7 +722,7 @@ static void *dec_worker(void *p) {
     uint64_t a = w->offsets[c], b = w->offsets[c + 1];
     int st = skvref_decode_chunk(w->m, w->sh, c, w->bits + a, b - a,
                                  (const uint8_t *)w->mu + g.base * mu_bytes(w->sh),
-                                 w->sigma + g.row * w->sh->head_dim,
+                                 w->sigma + g.row * w->sh->head_dim * sigma_stride(w->sh),
                                  (uint8_t *)w->x_out + g.base * sym_bytes(w->sh));
     if (st != REF_OK && w->status == REF_OK) w->status = st;
   }
@@ -766,12 +829,18 @@ int skvref_decode(const ref_shape *sh, const uint8_t *bits, const uint64_t *offs
 /*   S_c += RN64(r * r), r = RN64(v - mu'), in call order, then token order */
 /*   n_c += 1;  sigma_c = RN32(sqrt(RN64(S_c / n_c))), 1.0 when n_c = 0.    */
 /* p_hat's histogram counts every symbol pattern (NaNs included).           */
+/* Octave mode also sums per (channel, E(mu')), E the fp32 exponent field,  */
+/* into So / no (256 bins per channel), in the same order.                   */
 /* ------------------------------------------------------------------------ */
+#define EXP_BINS 256
+
 typedef struct {
   const ref_shape *sh;
   const void *x, *mu;
   double *S;
   uint64_t *n;
+  double *So;     /* octave mode: [channels][EXP_BINS], else NULL */
+  uint64_t *no;
   int64_t r0, r1;
 } cal_work;
 
@@ -788,10 +857,16 @@ static void *cal_worker(void *p) {
         int64_t i = (row * T + t) * D + d;
         double v = skvref_value(sh->sym_fmt, sym_at(sh->sym_fmt, w->x, i));
         if (!isfinite(v)) continue;
-        double r = v - (double)mu_prime(mu_at(sh->mu_fmt, w->mu, i));
+        float mp = mu_prime(mu_at(sh->mu_fmt, w->mu, i));
+        double r = v - (double)mp;
         double rr = r * r;
         S = S + rr;
         n++;
+        if (w->So) {
+          int64_t k = c * EXP_BINS + exp_field(mp);
+          w->So[k] = w->So[k] + rr;
+          w->no[k]++;
+        }
       }
       w->S[c] = S;
       w->n[c] = n;
@@ -801,7 +876,7 @@ static void *cal_worker(void *p) {
 }
 
 int skvref_calib_accumulate(const ref_shape *sh, const void *x, const void *mu, double *S,
-                            uint64_t *n, uint64_t *hist, int nthreads) {
+                            uint64_t *n, double *So, uint64_t *no, uint64_t *hist, int nthreads) {
   int e = shape_ok(sh);
   if (e != REF_OK) return e;
   int64_t rows = sh->layers * 2 * sh->kv_heads;
@@ -811,6 +886,8 @@ int skvref_calib_accumulate(const ref_shape *sh, const void *x, const void *mu, 
   pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
   for (int t = 0; t < nthreads; t++) {
     ws[t].sh = sh; ws[t].x = x; ws[t].mu = mu; ws[t].S = S; ws[t].n = n;
+    ws[t].So = sh->sigma_mode == REF_SIGMA_OCTAVE ? So : NULL;
+    ws[t].no = no;
     ws[t].r0 = rows * t / nthreads;
     ws[t].r1 = rows * (t + 1) / nthreads;
     pthread_create(&th[t], NULL, cal_worker, &ws[t]);
@@ -827,6 +904,28 @@ void skvref_calib_finalize(int64_t nch, const double *S, const uint64_t *n, floa
     if (n[c] == 0) { sigma[c] = 1.0f; continue; }
     double q = S[c] / (double)n[c];
     sigma[c] = (float)sqrt(q);
+  }
+}
+
+/* Octave mode: [0] = sigma_c as above; [1 + j] = the same estimator over the
+   channel's scalars in octave j (their exponent bins summed in increasing
+   exponent order), or sigma_c when fewer than OCT_MIN_COUNT fell there. */
+void skvref_calib_finalize_octave(int64_t nch, const double *S, const uint64_t *n, const double *So,
+                                  const uint64_t *no, float *table) {
+  for (int64_t c = 0; c < nch; c++) {
+    float sc = n[c] == 0 ? 1.0f : (float)sqrt(S[c] / (double)n[c]);
+    float *t = table + c * OCT_STRIDE;
+    t[0] = sc;
+    double Sj[OCTAVES] = {0};
+    uint64_t nj[OCTAVES] = {0};
+    for (int e = 0; e < EXP_BINS; e++) {
+      int j = e - (int)exp_field(sc > 0x1p-100f ? sc : 0x1p-100f) - 1;
+      j = j < 0 ? 0 : (j > OCTAVES - 1 ? OCTAVES - 1 : j);
+      Sj[j] = Sj[j] + So[c * EXP_BINS + e];
+      nj[j] += no[c * EXP_BINS + e];
+    }
+    for (int j = 0; j < OCTAVES; j++)
+      t[1 + j] = nj[j] < OCT_MIN_COUNT ? sc : (float)sqrt(Sj[j] / (double)nj[j]);
   }
 }
 

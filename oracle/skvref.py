@@ -20,6 +20,10 @@ LIB = os.path.join(HERE, "libskvref.so")
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLE = 0, 1, 2, 4, 5, 6
 SYM_BF16, SYM_E4M3 = 0, 1
 MU_BF16, MU_F32 = 0, 1
+SIGMA_CHANNEL, SIGMA_OCTAVE = 0, 1
+OCTAVES = 8
+OCT_STRIDE = 1 + OCTAVES  # octave-mode sigma table per channel: [sigma_c, sigma_c,0 .. sigma_c,7]
+EXP_BINS = 256
 
 
 def build(force: bool = False) -> str:
@@ -34,7 +38,8 @@ def build(force: bool = False) -> str:
 
 class Shape(C.Structure):
     _fields_ = [("layers", C.c_int64), ("kv_heads", C.c_int64), ("tokens", C.c_int64),
-                ("head_dim", C.c_int64), ("sym_fmt", C.c_int32), ("mu_fmt", C.c_int32)]
+                ("head_dim", C.c_int64), ("sym_fmt", C.c_int32), ("mu_fmt", C.c_int32),
+                ("sigma_mode", C.c_int32), ("reserved", C.c_int32)]
 
 
 _lib = None
@@ -72,8 +77,9 @@ def lib():
         L.skvref_encode_chunk.restype = u64
         L.skvref_encode_chunk.argtypes = [vp, vp, i64, vp, vp, vp, vp, u64, C.POINTER(C.c_int)]
         L.skvref_decode_chunk.argtypes = [vp, vp, i64, vp, u64, vp, vp, vp]
-        L.skvref_calib_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, C.c_int]
+        L.skvref_calib_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, C.c_int]
         L.skvref_calib_finalize.argtypes = [i64, vp, vp, vp]
+        L.skvref_calib_finalize_octave.argtypes = [i64, vp, vp, vp, vp, vp]
         L.skvref_rc_encode_seq.restype = u64
         L.skvref_rc_encode_seq.argtypes = [vp, vp, i64, vp, u64]
     return _lib
@@ -84,8 +90,9 @@ def _p(a: np.ndarray):
     return a.ctypes.data_as(C.c_void_p)
 
 
-def make_shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16) -> Shape:
-    return Shape(layers, kv_heads, tokens, head_dim, sym_fmt, mu_fmt)
+def make_shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16,
+               sigma_mode=SIGMA_CHANNEL) -> Shape:
+    return Shape(layers, kv_heads, tokens, head_dim, sym_fmt, mu_fmt, sigma_mode, 0)
 
 
 class Model:
@@ -243,22 +250,32 @@ def decode(shape: Shape, bits, offsets, mu, sigma, hist, nthreads=8):
 
 
 class Calibrator:
-    """sigma per (layer, kv, head, channel) and the symbol histogram."""
+    """sigma per (layer, kv, head, channel), or per channel and |mu| octave in
+    octave mode (a table of OCT_STRIDE floats per channel), and the symbol
+    histogram."""
 
     def __init__(self, shape: Shape):
         self.shape = shape
         nch = shape.layers * 2 * shape.kv_heads * shape.head_dim
         self.S = np.zeros(nch, dtype=np.float64)
         self.n = np.zeros(nch, dtype=np.uint64)
+        nb = nch * EXP_BINS if shape.sigma_mode == SIGMA_OCTAVE else 1
+        self.So = np.zeros(nb, dtype=np.float64)
+        self.no = np.zeros(nb, dtype=np.uint64)
         self.hist = np.zeros(65536 if shape.sym_fmt == SYM_BF16 else 256, dtype=np.uint64)
 
     def accumulate(self, x, mu, nthreads=8):
         st = lib().skvref_calib_accumulate(C.byref(self.shape), _p(x), _p(mu), _p(self.S), _p(self.n),
-                                           _p(self.hist), nthreads)
+                                           _p(self.So), _p(self.no), _p(self.hist), nthreads)
         if st != OK:
             raise RuntimeError(f"oracle calibration failed (status {st})")
 
     def finalize(self):
-        sigma = np.zeros(self.S.size, dtype=np.float32)
-        lib().skvref_calib_finalize(self.S.size, _p(self.S), _p(self.n), _p(sigma))
+        nch = self.S.size
+        if self.shape.sigma_mode == SIGMA_OCTAVE:
+            table = np.zeros(nch * OCT_STRIDE, dtype=np.float32)
+            lib().skvref_calib_finalize_octave(nch, _p(self.S), _p(self.n), _p(self.So), _p(self.no), _p(table))
+            return table, self.hist.copy()
+        sigma = np.zeros(nch, dtype=np.float32)
+        lib().skvref_calib_finalize(nch, _p(self.S), _p(self.n), _p(sigma))
         return sigma, self.hist.copy()
