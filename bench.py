@@ -86,9 +86,9 @@ def main():
     # ---- inputs in HBM (not timed)
     t0 = time.time()
     x, mu = synth.generate(w, device=dev)
-    csh = skv.shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+    csh = skv.shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
     state = torch.empty(skv.calib_state_size(csh), dtype=torch.uint8, device=dev)
-    sigma = torch.empty(w.n_channels, dtype=torch.float32, device=dev)
+    sigma = torch.empty(skv.sigma_floats(csh), dtype=torch.float32, device=dev)
     hist = torch.empty(65536 if w.sym_fmt == 0 else 256, dtype=torch.int64, device=dev)
     assert skv.calib_reset(state, csh) == skv.OK
     for j in range(nseq):
@@ -100,7 +100,7 @@ def main():
     print(f"# inputs ready in {time.time() - t0:.1f}s: {w.name}, {w.n_scalars} scalars, {nseq} calibration sequences",
           file=sys.stderr, flush=True)
 
-    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
     buf = skv.Buffers(sh, device=dev)
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
@@ -184,7 +184,8 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads, "tokens": w.tokens,
                    "head_dim": w.head_dim, "symbols": "bf16" if w.sym_fmt == 0 else "e4m3",
                    "mu": "bf16" if w.mu_fmt == 0 else "f32", "n_scalars": n, "calib_seqs": nseq,
-                   "calib_tokens": w.calib_tokens, "chunk_tokens": 256, "lanes_per_chunk": 64},
+                   "calib_tokens": w.calib_tokens, "chunk_tokens": 256, "lanes_per_chunk": 64,
+                   "sigma": "channel x |mu| octave" if w.sigma_mode else "channel"},
         "encode_GBps": round(enc_gbps, 3),
         "decode_GBps": round(dec_gbps, 3),
         "encode_ms": round(enc_ms, 4),
@@ -227,8 +228,8 @@ def cpu_baseline(w, x, mu, sigma, hist, buf, seconds):
     from oracle import skvref as R
 
     cores = max(1, min(os.cpu_count() or 1, 16))
-    rs = R.make_shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
     rsig = sigma.cpu().numpy()
+    per_ch = R.OCT_STRIDE if w.sigma_mode == R.SIGMA_OCTAVE else 1
     rhist = hist.cpu().numpy().view(np.uint64)
     model = R.Model(w.sym_fmt, rhist)
     ntb = (w.tokens + 255) // 256
@@ -240,12 +241,13 @@ def cpu_baseline(w, x, mu, sigma, hist, buf, seconds):
         ms = mu.reshape(-1, w.tokens, w.head_dim)[:n_rows].cpu().numpy()
         xs = np.ascontiguousarray(xs.view(np.uint16 if w.sym_fmt == 0 else np.uint8))
         ms = np.ascontiguousarray(ms.view(np.uint16) if w.mu_fmt == 0 else ms)
-        shp = R.make_shape(1, n_rows // 2, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt) if n_rows % 2 == 0 else None
+        shp = (R.make_shape(1, n_rows // 2, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
+               if n_rows % 2 == 0 else None)
         return xs, ms, shp
 
     def run(n_rows):
         xs, ms, shp = sample(n_rows)
-        sig = np.ascontiguousarray(rsig[: n_rows * w.head_dim])
+        sig = np.ascontiguousarray(rsig[: n_rows * w.head_dim * per_ch])
         t0 = time.perf_counter()
         bits, offs = model.encode(shp, xs, ms, sig, nthreads=cores)
         t1 = time.perf_counter()

@@ -56,7 +56,7 @@ extern "C" {
 
 enum skv_status {
   SKV_OK = 0,
-  SKV_ERR_ARG = 1,          /* bad argument (null pointer, bad shape, non-finite or negative sigma) */
+  SKV_ERR_ARG = 1,          /* bad argument (null pointer, bad shape or sigma mode, non-finite or negative sigma) */
   SKV_ERR_UNSUPPORTED = 2,  /* head_dim not a multiple of 8 dividing 512 */
   SKV_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
   SKV_ERR_CAPACITY = 4,     /* the compressed stream does not fit bits_cap */
@@ -67,13 +67,37 @@ enum skv_status {
 enum skv_sym_fmt { SKV_SYM_BF16 = 0, SKV_SYM_E4M3 = 1 };
 enum skv_mu_fmt { SKV_MU_BF16 = 0, SKV_MU_F32 = 1 };
 
+/*
+ * How sigma is resolved per scalar.
+ *   SKV_SIGMA_CHANNEL: one sigma per (layer, kv, head, channel); the sigma
+ *     array is fp32 [layers][2][kv_heads][head_dim] ("早期结果").
+ *   SKV_SIGMA_OCTAVE: sigma also depends on the magnitude of the scalar's mean,
+ *     which both ends know (the pages name a static per-channel sigma as a
+ *     cost, "下一步计划").  The sigma array is fp32
+ *     [layers][2][kv_heads][head_dim][SKV_OCT_STRIDE]: per channel its own
+ *     sigma_c, then sigma_c,j for octaves j = 0..7.  A scalar with mean mu'
+ *     (mu, or 0 when mu is not finite) takes octave
+ *       j = clamp(E(mu') - E(max(sigma_c, 2^-100)) - 1, 0, 7),
+ *     E the fp32 biased exponent field (0 for zero and subnormals), and codes
+ *     with sigma_c,j.  Calibration sets sigma_c as in channel mode and
+ *     sigma_c,j by the same estimator over the channel's scalars in octave j
+ *     (their squares summed per exponent field in fp64, the fields of an
+ *     octave added in increasing order), or sigma_c when fewer than 16 fell
+ *     in the octave.
+ */
+enum skv_sigma_mode { SKV_SIGMA_CHANNEL = 0, SKV_SIGMA_OCTAVE = 1 };
+#define SKV_OCTAVES 8
+#define SKV_OCT_STRIDE (1 + SKV_OCTAVES)
+
 typedef struct skv_shape {
-  int64_t layers;    /* >= 1 */
-  int64_t kv_heads;  /* >= 1 */
-  int64_t tokens;    /* >= 1; the last 256-token chunk of a row may be shorter */
-  int64_t head_dim;  /* multiple of 8 dividing 512 */
-  int32_t sym_fmt;   /* enum skv_sym_fmt: symbols are bf16 (uint16 patterns) or e4m3 (uint8 patterns) */
-  int32_t mu_fmt;    /* enum skv_mu_fmt: predictor means are bf16 (uint16 patterns) or fp32 */
+  int64_t layers;      /* >= 1 */
+  int64_t kv_heads;    /* >= 1 */
+  int64_t tokens;      /* >= 1; the last 256-token chunk of a row may be shorter */
+  int64_t head_dim;    /* multiple of 8 dividing 512 */
+  int32_t sym_fmt;     /* enum skv_sym_fmt: symbols are bf16 (uint16 patterns) or e4m3 (uint8 patterns) */
+  int32_t mu_fmt;      /* enum skv_mu_fmt: predictor means are bf16 (uint16 patterns) or fp32 */
+  int32_t sigma_mode;  /* enum skv_sigma_mode */
+  int32_t reserved;    /* must be 0 */
 } skv_shape;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -95,7 +119,8 @@ int skv_encode_bound(const skv_shape *shape, size_t *bytes);
 int skv_workspace_size(const skv_shape *shape, size_t *bytes);
 
 /* Device workspace (calibration state) needed by the calibration calls: per
- * channel an fp64 sum of squares and a u64 count, plus the u64 histogram. */
+ * channel an fp64 sum of squares and a u64 count, plus the u64 histogram; in
+ * octave mode also per channel 256 such pairs, one per exponent field of mu'. */
 int skv_calib_state_size(const skv_shape *shape, size_t *bytes);
 
 /* ---------------------------------------------------------------- calibration */
@@ -123,9 +148,9 @@ int skv_calib_reset(void *state, const skv_shape *shape, void *stream);
 int skv_calib_accumulate(void *state, const skv_shape *seq_shape, const void *x, const void *mu,
                          void *stream);
 
-/* sigma (device, fp32 [layers][2][kv_heads][head_dim]) and hist (device, u64
- * [65536] for bf16, [256] for e4m3, indexed by bit pattern, raw counts) from
- * the state.  The state is left unchanged. */
+/* sigma (device, fp32 [layers][2][kv_heads][head_dim], times SKV_OCT_STRIDE in
+ * octave mode) and hist (device, u64 [65536] for bf16, [256] for e4m3, indexed
+ * by bit pattern, raw counts) from the state.  The state is left unchanged. */
 int skv_calib_finalize(const void *state, const skv_shape *shape, float *sigma, uint64_t *hist,
                        void *stream);
 
@@ -140,8 +165,9 @@ int skv_calibrate(const skv_shape *seq_shape, int64_t n_seq, const void *x, cons
  * Encode a cache.
  *   x       (device) symbols, cache layout, bf16 or e4m3 patterns
  *   mu      (device) predictor means, cache layout, bf16 patterns or fp32
- *   sigma   (device) fp32 [layers][2][kv_heads][head_dim], finite and >= 0
- *           (sigma below 2^-100 is treated as 2^-100)
+ *   sigma   (device) fp32 [layers][2][kv_heads][head_dim] (channel mode) or
+ *           [..][head_dim][SKV_OCT_STRIDE] (octave mode), every entry finite
+ *           and >= 0 (sigma below 2^-100 is treated as 2^-100)
  *   hist    (device) u64 symbol histogram as produced by skv_calib_finalize
  *   bits    (device) output stream, bits_cap bytes (>= skv_encode_bound
  *           guarantees success); 16-byte aligned

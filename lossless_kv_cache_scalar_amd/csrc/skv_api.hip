@@ -30,6 +30,8 @@ int make_geo(const skv_shape *sh, Geo &g) {
   if (sh->layers < 1 || sh->kv_heads < 1 || sh->tokens < 1 || sh->head_dim < 1) return SKV_ERR_ARG;
   if (sh->sym_fmt != SKV_SYM_BF16 && sh->sym_fmt != SKV_SYM_E4M3) return SKV_ERR_ARG;
   if (sh->mu_fmt != SKV_MU_BF16 && sh->mu_fmt != SKV_MU_F32) return SKV_ERR_ARG;
+  if ((sh->sigma_mode != SKV_SIGMA_CHANNEL && sh->sigma_mode != SKV_SIGMA_OCTAVE) || sh->reserved != 0)
+    return SKV_ERR_ARG;
   // head_dim a power of two from 8 to 512: a lane's channels then repeat with
   // a period dividing kBatch
   if (sh->head_dim % 8 != 0 || 512 % sh->head_dim != 0) return SKV_ERR_UNSUPPORTED;
@@ -43,6 +45,7 @@ int make_geo(const skv_shape *sh, Geo &g) {
   g.n_chunks = g.rows * g.ntb;
   g.sym_fmt = sh->sym_fmt;
   g.mu_fmt = sh->mu_fmt;
+  g.octave = sh->sigma_mode == SKV_SIGMA_OCTAVE ? 1 : 0;
   g.N = sh->sym_fmt == SKV_SYM_BF16 ? 65536u : 256u;
   g.log2T = sh->sym_fmt == SKV_SYM_BF16 ? 24u : 16u;
   // one count per symbol; the rest split 0.98 : 0.02 between the Gaussian
@@ -56,7 +59,7 @@ int make_geo(const skv_shape *sh, Geo &g) {
 }
 
 struct Layout {
-  size_t knots, ptab, a16, abase, aflag, psum, uinv, etab, scale, flags, ctr, scratch, total;
+  size_t knots, ptab, a16, abase, aflag, psum, uinv, etab, scale, eref, flags, ctr, scratch, total;
 };
 
 Layout layout(const Geo &g) {
@@ -70,7 +73,8 @@ Layout layout(const Geo &g) {
   L.psum = o;  o = align_up(o + sizeof(uint64_t) * 64);
   L.uinv = o;  o = align_up(o + sizeof(float2) * (kNInv + 1));
   L.etab = o;  o = align_up(o + sizeof(float2) * 256);
-  L.scale = o; o = align_up(o + sizeof(float2) * (size_t)(g.rows * g.D));
+  L.scale = o; o = align_up(o + sizeof(float2) * (size_t)(g.rows * g.D) * (g.octave ? kOctaves : 1));
+  L.eref = o;  o = align_up(o + sizeof(int32_t) * (size_t)(g.octave ? g.rows * g.D : 1));
   L.flags = o; o = align_up(o + sizeof(uint64_t) * (size_t)g.n_chunks);
   L.ctr = o;   o = align_up(o + sizeof(uint32_t));
   L.scratch = o; o = align_up(o + (size_t)g.n_chunks * kLanes * g.lane_cap);
@@ -91,6 +95,7 @@ Workspace carve(const Geo &g, void *base) {
   w.uinv = reinterpret_cast<float2 *>(b + L.uinv);
   w.etab = reinterpret_cast<float2 *>(b + L.etab);
   w.scale = reinterpret_cast<float2 *>(b + L.scale);
+  w.eref = reinterpret_cast<int32_t *>(b + L.eref);
   w.flags = reinterpret_cast<uint64_t *>(b + L.flags);
   w.ctr = reinterpret_cast<uint32_t *>(b + L.ctr);
   w.scratch = b + L.scratch;
@@ -136,7 +141,7 @@ extern "C" int skv_calib_state_size(const skv_shape *shape, size_t *bytes) {
   int e = make_geo(shape, g);
   if (e != SKV_OK) return e;
   if (!bytes) return SKV_ERR_ARG;
-  *bytes = sizeof(uint64_t) * (size_t)(2 * g.rows * g.D + g.N);
+  *bytes = sizeof(uint64_t) * (size_t)(2 * g.rows * g.D * (g.octave ? 1 + kExpBins : 1) + g.N);
   return SKV_OK;
 }
 

@@ -7,7 +7,11 @@
 // one thread owns a channel and sums its fp64 squares in token order, and the
 // histogram uses integer atomics only.
 //
-// State layout: S (fp64 [channels]) | n (u64 [channels]) | hist (u64 [N]).
+// Octave mode (sigma per channel and octave of |mu'|) also keeps, per channel,
+// the same sums split by the fp32 exponent field of mu'.
+//
+// State layout: S (fp64 [channels]) | n (u64 [channels]) | hist (u64 [N]),
+// then in octave mode So (fp64 [channels][256]) | no (u64 [channels][256]).
 #include "skv_internal.hpp"
 
 namespace skv {
@@ -16,6 +20,8 @@ struct CalState {
   double *S;
   uint64_t *n;
   uint64_t *hist;
+  double *So;    // octave mode only
+  uint64_t *no;
 };
 
 static CalState cal_state(const Geo &g, void *state) {
@@ -24,6 +30,8 @@ static CalState cal_state(const Geo &g, void *state) {
   c.S = static_cast<double *>(state);
   c.n = reinterpret_cast<uint64_t *>(c.S + nch);
   c.hist = c.n + nch;
+  c.So = reinterpret_cast<double *>(c.hist + g.N);
+  c.no = reinterpret_cast<uint64_t *>(c.So + nch * kExpBins);
   return c;
 }
 
@@ -33,7 +41,8 @@ __global__ void k_fill_u64(uint64_t *p, int64_t n) {
 }
 
 hipError_t launch_calib_reset(const Geo &g, void *state, hipStream_t st) {
-  int64_t words = 2 * g.rows * g.D + g.N;  // S, n and hist are all 8-byte words
+  // S, n, hist (and So, no) are all 8-byte words
+  int64_t words = 2 * g.rows * g.D * (g.octave ? 1 + kExpBins : 1) + g.N;
   hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
                      static_cast<uint64_t *>(state), words);
   return hipGetLastError();
@@ -46,10 +55,12 @@ __device__ __forceinline__ double e4m3_value(uint32_t b) {
   return (b & 0x80u) ? -v : v;
 }
 
-// One thread per channel: over the call's tokens in order, S += RN(r * r).
-template <int SYM, int MU>
+// One thread per channel: over the call's tokens in order, S += RN(r * r);
+// in octave mode the same square also goes to the bin of mu's exponent field.
+template <int SYM, int MU, int OCT>
 __global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, const void *__restrict__ mu,
-                                                    double *__restrict__ S, uint64_t *__restrict__ n, int64_t rows,
+                                                    double *__restrict__ S, uint64_t *__restrict__ n,
+                                                    double *__restrict__ So, uint64_t *__restrict__ no, int64_t rows,
                                                     int64_t tokens, int64_t D) {
   int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= rows * D) return;
@@ -76,6 +87,11 @@ __global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, 
     double rr = r * r;
     acc = acc + rr;
     ++cnt;
+    if (OCT) {
+      const int64_t k = c * kExpBins + ((__float_as_uint(m) >> 23) & 0xFFu);
+      So[k] = So[k] + rr;
+      no[k] = no[k] + 1;
+    }
   }
   S[c] = acc;
   n[c] = cnt;
@@ -113,17 +129,20 @@ hipError_t launch_calib_accumulate(const Geo &g, void *state, const void *x, con
   CalState cs = cal_state(g, state);
   int64_t nch = g.rows * g.D;
   dim3 grid((unsigned)((nch + 255) / 256)), blk(256);
-  if (g.sym_fmt == SKV_SYM_BF16) {
-    if (g.mu_fmt == SKV_MU_BF16)
-      hipLaunchKernelGGL((k_calib_sums<SKV_SYM_BF16, SKV_MU_BF16>), grid, blk, 0, st, x, mu, cs.S, cs.n, g.rows, g.tokens, g.D);
-    else
-      hipLaunchKernelGGL((k_calib_sums<SKV_SYM_BF16, SKV_MU_F32>), grid, blk, 0, st, x, mu, cs.S, cs.n, g.rows, g.tokens, g.D);
-  } else {
-    if (g.mu_fmt == SKV_MU_BF16)
-      hipLaunchKernelGGL((k_calib_sums<SKV_SYM_E4M3, SKV_MU_BF16>), grid, blk, 0, st, x, mu, cs.S, cs.n, g.rows, g.tokens, g.D);
-    else
-      hipLaunchKernelGGL((k_calib_sums<SKV_SYM_E4M3, SKV_MU_F32>), grid, blk, 0, st, x, mu, cs.S, cs.n, g.rows, g.tokens, g.D);
+  const int sel = (g.sym_fmt == SKV_SYM_BF16 ? 0 : 4) + (g.mu_fmt == SKV_MU_BF16 ? 0 : 2) + g.octave;
+#define SKV_SUMS(S_, M_, O_) \
+  hipLaunchKernelGGL((k_calib_sums<S_, M_, O_>), grid, blk, 0, st, x, mu, cs.S, cs.n, cs.So, cs.no, g.rows, g.tokens, g.D)
+  switch (sel) {
+    case 0: SKV_SUMS(SKV_SYM_BF16, SKV_MU_BF16, 0); break;
+    case 1: SKV_SUMS(SKV_SYM_BF16, SKV_MU_BF16, 1); break;
+    case 2: SKV_SUMS(SKV_SYM_BF16, SKV_MU_F32, 0); break;
+    case 3: SKV_SUMS(SKV_SYM_BF16, SKV_MU_F32, 1); break;
+    case 4: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_BF16, 0); break;
+    case 5: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_BF16, 1); break;
+    case 6: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_F32, 0); break;
+    default: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_F32, 1); break;
   }
+#undef SKV_SUMS
   int64_t total = g.rows * g.tokens * g.D;
   dim3 hgrid((unsigned)((total + kHistTile - 1) / kHistTile)), hblk(1024);
   if (g.sym_fmt == SKV_SYM_BF16) {
@@ -171,12 +190,44 @@ __global__ void k_calib_finalize(const double *__restrict__ S, const uint64_t *_
   if (i < N) hist_out[i] = hist_in[i];
 }
 
+// Octave mode: per channel its sigma_c (as above), then per octave j the
+// estimator over the exponent bins that fall in j (see skv.h), added in
+// increasing exponent order, or sigma_c below 16 scalars.
+__global__ void k_calib_finalize_oct(const double *__restrict__ S, const uint64_t *__restrict__ n,
+                                     const double *__restrict__ So, const uint64_t *__restrict__ no,
+                                     float *__restrict__ table, int64_t nch) {
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nch) return;
+  const float sc = n[c] == 0 ? 1.0f : rn32_sqrt(S[c] / (double)n[c]);
+  float *t = table + c * SKV_OCT_STRIDE;
+  t[0] = sc;
+  const int base = (int)((__float_as_uint(sc > 0x1p-100f ? sc : 0x1p-100f) >> 23) & 0xFFu) + 1;
+  const double *so = So + c * kExpBins;
+  const uint64_t *nn = no + c * kExpBins;
+  for (int j = 0; j < kOctaves; ++j) {
+    // exponent fields of octave j: [0, base] for j = 0, base + j for 0 < j < 7, [base + 7, 255] for j = 7
+    const int e0 = j == 0 ? 0 : base + j;
+    const int e1 = j == kOctaves - 1 ? kExpBins - 1 : (j == 0 ? base : base + j);
+    double sj = 0.0;
+    uint64_t nj = 0;
+    for (int e = e0; e <= e1 && e < kExpBins; ++e) {
+      sj = sj + so[e];
+      nj += nn[e];
+    }
+    t[1 + j] = nj < 16 ? sc : rn32_sqrt(sj / (double)nj);
+  }
+}
+
 hipError_t launch_calib_finalize(const Geo &g, const void *state, float *sigma, uint64_t *hist, hipStream_t st) {
   CalState cs = cal_state(g, const_cast<void *>(state));
   int64_t nch = g.rows * g.D;
   int64_t m = nch > (int64_t)g.N ? nch : (int64_t)g.N;
-  hipLaunchKernelGGL(k_calib_finalize, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, cs.S, cs.n, cs.hist, sigma,
-                     hist, nch, (int64_t)g.N);
+  // channel sigmas (overwritten by the octave tables below in octave mode) and the histogram
+  hipLaunchKernelGGL(k_calib_finalize, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, cs.S, cs.n, cs.hist,
+                     g.octave ? nullptr : sigma, hist, g.octave ? 0 : nch, (int64_t)g.N);
+  if (g.octave)
+    hipLaunchKernelGGL(k_calib_finalize_oct, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, cs.S, cs.n, cs.So,
+                       cs.no, sigma, nch);
   return hipGetLastError();
 }
 

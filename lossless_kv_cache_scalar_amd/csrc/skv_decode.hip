@@ -40,7 +40,8 @@ struct DecArgs {
   const int32_t *aflag;
   const float2 *uinv;
   const float2 *etab;
-  const float2 *scale;
+  const float2 *scale;   // per channel, or per channel and octave
+  const int32_t *eref;   // octave mode: per channel octave reference
   float inv_step;  // kNInv / MG
   void *x_out;
   int32_t *status;
@@ -369,7 +370,6 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
                                                   bool &corrupt, float m, uint32_t mraw, float sj, float sinvj) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   constexpr int up = BF ? 0 : 8;
-  constexpr uint32_t N = BF ? 65536u : 256u;
   const uint32_t r = (uint32_t)(range >> 24);
   // ---- guess: invert the Gaussian pair's CDF at t - A(k), first with k the
   // rank of mu, then with k the rank of that first guess (the one-count floor
@@ -397,7 +397,7 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   return gs;
 }
 
-template <int SYM, int MU, int PER, int TAB>
+template <int SYM, int MU, int PER, int OCT, int TAB>
 __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs &t, const float2 *uinv) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   const Geo &g = a.g;
@@ -450,16 +450,27 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     // k has channel (l + 64 k) mod D, which repeats with period PER = max(2, D / 64),
     // a divisor of kBatch
     float s[PER], sinv[PER];
+    int32_t er[PER];  // octave mode: the channels' octave references
+    uint32_t cb[PER]; // octave mode: the channels' first table entries
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const float2 sc = a.scale[row * g.D + ((lane + kLanes * j) & (D - 1))];
-      s[j] = sc.x;
-      sinv[j] = sc.y;
+      const int64_t ch = row * g.D + ((lane + kLanes * j) & (D - 1));
+      if (OCT) {
+        er[j] = a.eref[ch];
+        cb[j] = (uint32_t)(ch * kOctaves);
+      } else {
+        const float2 sc = a.scale[ch];
+        s[j] = sc.x;
+        sinv[j] = sc.y;
+      }
     }
     // wait for the scales here: a wait inside the symbol loop would also wait
     // for the loads in flight on every trip
 #pragma unroll
-    for (int j = 0; j < PER; ++j) asm volatile("" ::"v"(s[j]), "v"(sinv[j]));
+    for (int j = 0; j < PER; ++j) {
+      if (OCT) asm volatile("" ::"v"(er[j]));
+      else asm volatile("" ::"v"(s[j]), "v"(sinv[j]));
+    }
     const void *mu_ch = MU == SKV_MU_BF16 ? (const void *)(static_cast<const uint16_t *>(a.mu) + base)
                                           : (const void *)(static_cast<const float *>(a.mu) + base);
     void *x_ch = BF ? (void *)(static_cast<uint16_t *>(a.x_out) + base) : (void *)(static_cast<uint8_t *>(a.x_out) + base);
@@ -478,10 +489,16 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.v[j]));
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
+      // octave mode: the batch's scales, read at its start (the means are here)
+      float2 sb[kBatch];
+      if (OCT) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) sb[j] = a.scale[cb[j % PER] + octave_of(cur.get(j), er[j % PER])];
+      }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, cur.get(j), cur.v[j],
-                                                        s[j % PER], sinv[j % PER]);
+                                                        OCT ? sb[j].x : s[j % PER], OCT ? sb[j].y : sinv[j % PER]);
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
         else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
@@ -492,16 +509,33 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     for (int k = nfull * kBatch; k < nk; ++k) {
       const uint32_t i = (uint32_t)lane + (uint32_t)k * kLanes;
       const int j = k & (kBatch - 1);
-      float sj = s[0], sij = sinv[0];
-#pragma unroll
-      for (int q = 1; q < PER; ++q) {
-        if (j % PER == q) {
-          sj = s[q];
-          sij = sinv[q];
-        }
-      }
       const uint32_t mraw = cur.one(mu_ch, i);
       const float m = MU == SKV_MU_BF16 ? mu_from_bf16(mraw) : mu_from_f32(__uint_as_float(mraw));
+      float sj, sij;
+      if (OCT) {
+        int32_t e = er[0];
+        uint32_t b0 = cb[0];
+#pragma unroll
+        for (int q = 1; q < PER; ++q) {
+          if (j % PER == q) {
+            e = er[q];
+            b0 = cb[q];
+          }
+        }
+        const float2 sc = a.scale[b0 + octave_of(m, e)];
+        sj = sc.x;
+        sij = sc.y;
+      } else {
+        sj = s[0];
+        sij = sinv[0];
+#pragma unroll
+        for (int q = 1; q < PER; ++q) {
+          if (j % PER == q) {
+            sj = s[q];
+            sij = sinv[q];
+          }
+        }
+      }
       const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, m, mraw, sj, sij);
       br.issue();
       if (BF) static_cast<uint16_t *>(x_ch)[i] = (uint16_t)gs;
@@ -513,7 +547,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
   }
 }
 
-template <int SYM, int MU, int PER>
+template <int SYM, int MU, int PER, int OCT>
 __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   __shared__ float2 s_kn[kNKnot];
@@ -537,8 +571,8 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   }
   __syncthreads();
   const ModelTabs t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, a.ptab, s_et};
-  if (!BF || win) decode_chunks<SYM, MU, PER, kTabLdsAll>(a, t, s_ui);
-  else decode_chunks<SYM, MU, PER, kTabGlobal>(a, t, s_ui);
+  if (!BF || win) decode_chunks<SYM, MU, PER, OCT, kTabLdsAll>(a, t, s_ui);
+  else decode_chunks<SYM, MU, PER, OCT, kTabGlobal>(a, t, s_ui);
 }
 
 static int dec_cu_count() {
@@ -557,16 +591,21 @@ static void launch_dec_kernel(const DecArgs &a, hipStream_t st) {
   const int64_t need = (a.g.n_chunks + kDecWaves - 1) / kDecWaves;
   const int64_t cus = dec_cu_count();
   const unsigned blocks = (unsigned)(need < cus ? need : cus);
-  // the scale period of a lane's symbols: max(2, head_dim / 64)
-  if (a.g.D >= 512) hipLaunchKernelGGL((k_decode<SYM, MU, 8>), dim3(blocks), dim3(kDecBlock), 0, st, a);
-  else if (a.g.D >= 256) hipLaunchKernelGGL((k_decode<SYM, MU, 4>), dim3(blocks), dim3(kDecBlock), 0, st, a);
-  else hipLaunchKernelGGL((k_decode<SYM, MU, 2>), dim3(blocks), dim3(kDecBlock), 0, st, a);
+  // the scale period of a lane's symbols: max(2, head_dim / 64); the sigma mode
+#define SKV_DEC(P_, O_) hipLaunchKernelGGL((k_decode<SYM, MU, P_, O_>), dim3(blocks), dim3(kDecBlock), 0, st, a)
+  const int per = a.g.D >= 512 ? 8 : (a.g.D >= 256 ? 4 : 2);
+  if (a.g.octave) {
+    if (per == 8) SKV_DEC(8, 1); else if (per == 4) SKV_DEC(4, 1); else SKV_DEC(2, 1);
+  } else {
+    if (per == 8) SKV_DEC(8, 0); else if (per == 4) SKV_DEC(4, 0); else SKV_DEC(2, 0);
+  }
+#undef SKV_DEC
 }
 
 hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes, const uint64_t *offsets,
                          const void *mu, const Workspace &ws, void *x_out, int32_t *status, hipStream_t st) {
   DecArgs a{g, bits, bits_bytes, offsets, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.uinv, ws.etab,
-            ws.scale, (float)kNInv / (float)g.MG, x_out, status};
+            ws.scale, ws.eref, (float)kNInv / (float)g.MG, x_out, status};
   timing_mark(kTimeDecode, false, st);
   if (g.sym_fmt == SKV_SYM_BF16) {
     if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_BF16, SKV_MU_BF16>(a, st);

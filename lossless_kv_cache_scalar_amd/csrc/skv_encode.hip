@@ -33,7 +33,8 @@ struct EncArgs {
   const uint32_t *abase;
   const int32_t *aflag;
   const float2 *etab;
-  const float2 *scale;
+  const float2 *scale;  // per channel, or per channel and octave
+  const int32_t *eref;   // octave mode: per channel octave reference
   uint64_t *flags;  // per chunk: kFlagAgg | size, then kFlagIncl | offset + size
   uint32_t *ctr;    // next chunk id
   uint8_t *scratch;
@@ -353,7 +354,7 @@ __device__ __forceinline__ void model_pair(const EncArgs &a, const EncTables &t,
   }
 }
 
-template <int SYM, int MU, int PER, bool FAST>
+template <int SYM, int MU, int PER, int OCT, bool FAST>
 __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables &t) {
   const Geo &g = a.g;
   const int lane = threadIdx.x & 63;
@@ -401,12 +402,25 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     // symbol k of the lane has channel (lane + 64 k) mod D; with D a power of
     // two up to 512 that repeats with period PER = max(2, D / 64), which divides kBatch
     float s[PER];
+    int32_t er[PER];  // octave mode: the channels' octave references
+    uint32_t cb[PER]; // octave mode: the channels' first table entries
 #pragma unroll
-    for (int j = 0; j < PER; ++j) s[j] = a.scale[row * g.D + ((lane + kLanes * j) & (D - 1))].x;
+    for (int j = 0; j < PER; ++j) {
+      const int64_t ch = row * g.D + ((lane + kLanes * j) & (D - 1));
+      if (OCT) {
+        er[j] = a.eref[ch];
+        cb[j] = (uint32_t)(ch * kOctaves);
+      } else {
+        s[j] = a.scale[ch].x;
+      }
+    }
     // wait for the scales here: a wait inside the symbol loop would also wait
     // for the batch loads in flight on every trip
 #pragma unroll
-    for (int j = 0; j < PER; ++j) asm volatile("" ::"v"(s[j]));
+    for (int j = 0; j < PER; ++j) {
+      if (OCT) asm volatile("" ::"v"(er[j]));
+      else asm volatile("" ::"v"(s[j]));
+    }
 
     LaneCoder cod;
     cod.init(a.scratch + (uint64_t)chunk * kLanes * g.lane_cap, (uint32_t)lane, g.lane_cap / 4);
@@ -425,10 +439,16 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
       if (b + 1 < nfull) nxt.load_full(a, base + lane + (int64_t)(b + 1) * kStep);  // in flight meanwhile
+      // octave mode: the batch's scales, read at its start (the means are here)
+      float sb[kBatch];
+      if (OCT) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) sb[j] = a.scale[cb[j % PER] + octave_of(cur.mu(j), er[j % PER])].x;
+      }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         uint32_t c, f;
-        model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), s[j % PER], c, f);
+        model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), OCT ? sb[j] : s[j % PER], c, f);
         cod.encode(c, f);
       }
       cur = nxt;
@@ -437,11 +457,24 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     for (int k = nfull * kBatch; k < nk; ++k) {
       const int64_t i = base + lane + (int64_t)k * kLanes;
       const int j = k & (kBatch - 1);
-      float sj = s[0];
-#pragma unroll
-      for (int q = 1; q < PER; ++q)
-        if (j % PER == q) sj = s[q];
       cur.one(a, i, 0);
+      float sj;
+      if (OCT) {
+        int32_t e = er[0];
+        uint32_t b0 = cb[0];
+#pragma unroll
+        for (int q = 1; q < PER; ++q)
+          if (j % PER == q) {
+            e = er[q];
+            b0 = cb[q];
+          }
+        sj = a.scale[b0 + octave_of(cur.mu(0), e)].x;
+      } else {
+        sj = s[0];
+#pragma unroll
+        for (int q = 1; q < PER; ++q)
+          if (j % PER == q) sj = s[q];
+      }
       uint32_t c, f;
       model_pair<SYM, FAST>(a, t, cur.xs[0], cur.mu(0), sj, c, f);
       cod.encode(c, f);
@@ -480,7 +513,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
   }
 }
 
-template <int SYM, int MU, int PER>
+template <int SYM, int MU, int PER, int OCT>
 __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   __shared__ float2 s_kn[kNKnot];
@@ -502,8 +535,8 @@ __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   }
   __syncthreads();
   const EncTables t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, s_et};
-  if (fast) encode_chunks<SYM, MU, PER, true>(a, t);
-  else encode_chunks<SYM, MU, PER, false>(a, t);
+  if (fast) encode_chunks<SYM, MU, PER, OCT, true>(a, t);
+  else encode_chunks<SYM, MU, PER, OCT, false>(a, t);
 }
 
 __global__ void k_enc_reset(uint64_t *__restrict__ flags, int64_t n, uint32_t *__restrict__ ctr) {
@@ -528,15 +561,20 @@ static void launch_enc_kernel(const EncArgs &a, hipStream_t st) {
   const int64_t need = (a.g.n_chunks + kEncWaves - 1) / kEncWaves;
   const int64_t cus = cu_count();
   const unsigned blocks = (unsigned)(need < cus ? need : cus);
-  // the scale period of a lane's symbols: max(2, head_dim / 64)
-  if (a.g.D >= 512) hipLaunchKernelGGL((k_encode<SYM, MU, 8>), dim3(blocks), dim3(kEncBlock), 0, st, a);
-  else if (a.g.D >= 256) hipLaunchKernelGGL((k_encode<SYM, MU, 4>), dim3(blocks), dim3(kEncBlock), 0, st, a);
-  else hipLaunchKernelGGL((k_encode<SYM, MU, 2>), dim3(blocks), dim3(kEncBlock), 0, st, a);
+  // the scale period of a lane's symbols: max(2, head_dim / 64); the sigma mode
+#define SKV_ENC(P_, O_) hipLaunchKernelGGL((k_encode<SYM, MU, P_, O_>), dim3(blocks), dim3(kEncBlock), 0, st, a)
+  const int per = a.g.D >= 512 ? 8 : (a.g.D >= 256 ? 4 : 2);
+  if (a.g.octave) {
+    if (per == 8) SKV_ENC(8, 1); else if (per == 4) SKV_ENC(4, 1); else SKV_ENC(2, 1);
+  } else {
+    if (per == 8) SKV_ENC(8, 0); else if (per == 4) SKV_ENC(4, 0); else SKV_ENC(2, 0);
+  }
+#undef SKV_ENC
 }
 
 hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Workspace &ws, uint8_t *bits,
                          uint64_t bits_cap, uint64_t *offsets, int32_t *status, hipStream_t st) {
-  EncArgs a{g, x, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.etab, ws.scale, ws.flags, ws.ctr,
+  EncArgs a{g, x, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.etab, ws.scale, ws.eref, ws.flags, ws.ctr,
             ws.scratch, bits, bits_cap, offsets, status};
   hipLaunchKernelGGL(k_enc_reset, dim3(256), dim3(256), 0, st, ws.flags, g.n_chunks, ws.ctr);
   timing_mark(kTimeEncode, false, st);

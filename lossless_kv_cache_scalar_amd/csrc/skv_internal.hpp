@@ -32,6 +32,8 @@ constexpr int kWinEntries = kWinRanks + 1;
 constexpr int kNWin = 65536 / kWinRanks;
 // inverse of the Gaussian-pair CDF (counts -> knot coordinate), decoder guesses
 constexpr int kNInv = 1024;
+constexpr int kOctaves = SKV_OCTAVES;
+constexpr int kExpBins = 256;  // fp32 exponent fields (calibration bins in octave mode)
 constexpr uint64_t kW48 = 0xFFFFFFFFFFFFull;
 constexpr uint64_t kTop40 = 1ull << 40;
 
@@ -42,6 +44,7 @@ struct Geo {
   int64_t rows;      // layers * 2 * heads
   int64_t n_chunks;
   int sym_fmt, mu_fmt;
+  int octave;        // sigma per (channel, octave of |mu'|) instead of per channel
   uint32_t N;        // alphabet: 65536 or 256
   uint32_t log2T;    // 24 or 16
   uint32_t MG, Mp;   // Gaussian-pair and p_hat budgets, MG + Mp = 2^log2T - N
@@ -64,7 +67,8 @@ struct Workspace {
   uint64_t *psum;     // per 1024 ranks: sum of hist + 1 (table build)
   float2 *uinv;       // kNInv + 1: (u, du) at y = m * MG / kNInv
   float2 *etab;       // 256 e4m3 bins (lo, hi), indexed by pattern
-  float2 *scale;      // per channel: (s, ~1/s), s = RN32(64 / max(sigma, 2^-100))
+  float2 *scale;      // per channel (octave mode: per channel and octave): (s, ~1/s), s = RN32(64 / max(sigma, 2^-100))
+  int32_t *eref;      // octave mode, per channel: E(max(sigma_c, 2^-100)) + 1; octave = clamp(E(mu') - eref, 0, 7)
   uint64_t *flags;    // n_chunks published sizes / prefixes (encode)
   uint32_t *ctr;      // next chunk id (encode)
   uint8_t *scratch;   // n_chunks * 64 * lane_cap (encode)
@@ -110,6 +114,12 @@ __device__ __forceinline__ float bf16_lo_edge(uint32_t b) {
   float lo, hi;
   bf16_bin(b, lo, hi);
   return lo;
+}
+
+// octave of a scalar with finite mean m in a channel with reference eref
+__device__ __forceinline__ uint32_t octave_of(float m, int32_t eref) {
+  const int32_t e = (int32_t)((__float_as_uint(m) >> 23) & 0xFFu);
+  return (uint32_t)min(max(e - eref, 0), kOctaves - 1);
 }
 
 // predictor mean in fp32; a non-finite mean reads as 0

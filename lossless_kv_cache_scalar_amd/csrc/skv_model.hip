@@ -214,6 +214,34 @@ __global__ void k_scale(const float *__restrict__ sigma, float2 *__restrict__ sc
   scale[i] = make_float2(sc, __builtin_amdgcn_rcpf(sc));
 }
 
+// Octave mode: per channel c (one thread), eref = E(max(sigma_c, 2^-100)) + 1
+// and the (s, ~1/s) of its eight octave sigmas, from the SKV_OCT_STRIDE table.
+__global__ void k_scale_oct(const float *__restrict__ table, float2 *__restrict__ scale, int32_t *__restrict__ eref,
+                            int64_t nch, int32_t *status) {
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nch) return;
+  const float *t = table + c * SKV_OCT_STRIDE;
+  bool bad = false;
+  float sg0 = t[0];
+  if (!(sg0 >= 0.0f) || !__builtin_isfinite(sg0)) {
+    bad = true;
+    sg0 = 1.0f;
+  }
+  const float sp0 = sg0 > 0x1p-100f ? sg0 : 0x1p-100f;
+  eref[c] = (int32_t)((__float_as_uint(sp0) >> 23) & 0xFFu) + 1;
+  for (int j = 0; j < kOctaves; ++j) {
+    float sg = t[1 + j];
+    if (!(sg >= 0.0f) || !__builtin_isfinite(sg)) {
+      bad = true;
+      sg = 1.0f;
+    }
+    const float sp = sg > 0x1p-100f ? sg : 0x1p-100f;
+    const float sc = (float)(64.0 / (double)sp);
+    scale[c * kOctaves + j] = make_float2(sc, __builtin_amdgcn_rcpf(sc));
+  }
+  if (bad) set_status(status, SKV_ERR_ARG);
+}
+
 __global__ void k_clear_status(int32_t *status) {
   if (threadIdx.x == 0) *status = SKV_OK;
 }
@@ -235,7 +263,11 @@ hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, 
   hipLaunchKernelGGL(k_uinv, dim3(1), dim3(1024), 0, st, ws.knots, ws.uinv, g.MG);
   if (g.sym_fmt == SKV_SYM_E4M3) hipLaunchKernelGGL(k_etab, dim3(1), dim3(256), 0, st, ws.etab);
   int64_t nch = g.rows * g.D;
-  hipLaunchKernelGGL(k_scale, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, sigma, ws.scale, nch, status);
+  if (g.octave)
+    hipLaunchKernelGGL(k_scale_oct, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, sigma, ws.scale, ws.eref,
+                       nch, status);
+  else
+    hipLaunchKernelGGL(k_scale, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, sigma, ws.scale, nch, status);
   timing_mark(kTimeModel, true, st);
   return hipGetLastError();
 }

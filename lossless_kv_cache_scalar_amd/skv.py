@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(HERE, "_lib", "libskv.so")
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLE = range(7)
 SYM_BF16, SYM_E4M3 = 0, 1
 MU_BF16, MU_F32 = 0, 1
+SIGMA_CHANNEL, SIGMA_OCTAVE = 0, 1
+OCTAVES = 8
+OCT_STRIDE = 1 + OCTAVES
 
 # every function skv.h declares, in declaration order
 EXPORTS = ["skv_status_string", "skv_num_chunks", "skv_encode_bound", "skv_workspace_size",
@@ -28,7 +31,8 @@ EXPORTS = ["skv_status_string", "skv_num_chunks", "skv_encode_bound", "skv_works
 
 class SkvShape(C.Structure):
     _fields_ = [("layers", C.c_int64), ("kv_heads", C.c_int64), ("tokens", C.c_int64),
-                ("head_dim", C.c_int64), ("sym_fmt", C.c_int32), ("mu_fmt", C.c_int32)]
+                ("head_dim", C.c_int64), ("sym_fmt", C.c_int32), ("mu_fmt", C.c_int32),
+                ("sigma_mode", C.c_int32), ("reserved", C.c_int32)]
 
 
 class SkvError(RuntimeError):
@@ -70,8 +74,15 @@ def load():
     return L
 
 
-def shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16) -> SkvShape:
-    return SkvShape(int(layers), int(kv_heads), int(tokens), int(head_dim), int(sym_fmt), int(mu_fmt))
+def shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16, sigma_mode=SIGMA_CHANNEL) -> SkvShape:
+    return SkvShape(int(layers), int(kv_heads), int(tokens), int(head_dim), int(sym_fmt), int(mu_fmt),
+                    int(sigma_mode), 0)
+
+
+def sigma_floats(sh: SkvShape) -> int:
+    """Length of the sigma array for a shape: one per channel, or OCT_STRIDE per channel in octave mode."""
+    nch = sh.layers * 2 * sh.kv_heads * sh.head_dim
+    return nch * (OCT_STRIDE if sh.sigma_mode == SIGMA_OCTAVE else 1)
 
 
 def status_string(code: int) -> str:
@@ -196,10 +207,9 @@ def timing_stop(capacity: int = 1 << 16):
 
 def calibrate_sequences(seq_shape: SkvShape, seqs, device="cuda", stream=None):
     """sigma and hist from an iterable of (x, mu) device tensors, each of seq_shape."""
-    nch = seq_shape.layers * 2 * seq_shape.kv_heads * seq_shape.head_dim
     nsym = 65536 if seq_shape.sym_fmt == SYM_BF16 else 256
     state = torch.empty(calib_state_size(seq_shape), dtype=torch.uint8, device=device)
-    sigma = torch.empty(nch, dtype=torch.float32, device=device)
+    sigma = torch.empty(sigma_floats(seq_shape), dtype=torch.float32, device=device)
     hist = torch.empty(nsym, dtype=torch.int64, device=device)
     _check(calib_reset(state, seq_shape, stream), "skv_calib_reset")
     for x, mu in seqs:

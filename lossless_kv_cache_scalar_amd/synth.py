@@ -53,6 +53,7 @@ class Workload:
     calib_seqs: int
     calib_tokens: int
     mu_kind: str = "mixture"  # "mixture": x + sigma_c r; "fp8block": block-FP8 round trip of x
+    sigma_mode: int = 0       # how the coder resolves sigma: 0 per channel, 1 per channel and |mu| octave
 
     @property
     def model_seed(self) -> int:
@@ -84,7 +85,7 @@ class Workload:
     def with_tokens(self, tokens: int, layers: int | None = None, name: str | None = None) -> "Workload":
         return Workload(name or self.name, self.index, layers or self.layers, self.kv_heads, self.head_dim,
                         tokens, self.sym_fmt, self.mu_fmt, self.sigma_k, self.calib_seqs, self.calib_tokens,
-                        self.mu_kind)
+                        self.mu_kind, self.sigma_mode)
 
 
 WORKLOADS = {
@@ -102,6 +103,8 @@ WORKLOADS = {
         Workload("qwen3_32b_e4m3_32k", 5, 64, 8, 128, 32768, SYM_E4M3, MU_BF16, 0.04, 128, 512),
         # Qwen3-32B geometry with an FP8-quantized copy of the cache as the predictor
         Workload("qwen3_32b_bf16_fp8res", 6, 64, 8, 128, 8192, SYM_BF16, MU_BF16, 0.0, 128, 512, "fp8block"),
+        # the same data coded with sigma per channel and octave of |mu| (same seeds)
+        Workload("qwen3_32b_bf16_fp8res_oct", 6, 64, 8, 128, 8192, SYM_BF16, MU_BF16, 0.0, 128, 512, "fp8block", 1),
     ]
 }
 

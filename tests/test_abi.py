@@ -60,6 +60,26 @@ def test_bad_shapes_rejected(lib, bad, code):
     assert lib.skv_encode(C.byref(skv.shape(*bad)), *([None] * 5), 0, None, None, 0, None, None) == code
 
 
+def test_sigma_mode_checks_and_sizes(lib):
+    """The sigma mode is validated (and the reserved word must be 0); octave
+    mode adds 256 fp64/u64 bin pairs per channel to the calibration state and a
+    scale per channel and octave to the workspace; the chunking is unchanged."""
+    import ctypes as C
+    n = C.c_int64(0)
+    bad = skv.shape(1, 1, 256, 64, 0, 0, 2)
+    assert lib.skv_num_chunks(C.byref(bad), C.byref(n)) == skv.ERR_ARG
+    bad = skv.shape(1, 1, 256, 64)
+    bad.reserved = 1
+    assert lib.skv_num_chunks(C.byref(bad), C.byref(n)) == skv.ERR_ARG
+    ch, oc = skv.shape(2, 4, 300, 128), skv.shape(2, 4, 300, 128, 0, 0, skv.SIGMA_OCTAVE)
+    nch = 2 * 2 * 4 * 128
+    assert skv.num_chunks(oc) == skv.num_chunks(ch) and skv.encode_bound(oc) == skv.encode_bound(ch)
+    assert skv.calib_state_size(oc) == skv.calib_state_size(ch) + 16 * 256 * nch
+    assert skv.workspace_size(oc) >= skv.workspace_size(ch) + 8 * 7 * nch
+    assert skv.sigma_floats(oc) == 9 * nch and skv.sigma_floats(ch) == nch
+    assert R.num_chunks(R.make_shape(2, 4, 300, 128, 0, 0, R.SIGMA_OCTAVE)) == skv.num_chunks(oc)
+
+
 def test_null_pointers_rejected(lib):
     sh = skv.shape(1, 2, 256, 64)
     assert skv.encode(sh, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, stream=0) == skv.ERR_ARG

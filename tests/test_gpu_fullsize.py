@@ -14,7 +14,8 @@ from gpu_util import DEV, ensure_built, np_mu, np_sym
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k", "qwen3_32b_bf16_fp8res"]
+NAMES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k", "qwen3_32b_bf16_fp8res",
+         "qwen3_32b_bf16_fp8res_oct"]
 CALIB_SEQS = 2  # the launch configuration does not depend on the calibration set's size
 
 
@@ -28,12 +29,12 @@ def test_full_size_roundtrip_and_sampled_oracle_parity(name):
     w = synth.WORKLOADS[name]
     print(f"[fullsize] {name}: {w.n_scalars} scalars", flush=True)
     ns = min(CALIB_SEQS, w.calib_seqs)
-    csh = skv.shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+    csh = skv.shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
     seqs = [synth.calibration_set(w, j, device=DEV) for j in range(ns)]
     sigma, hist = skv.calibrate_sequences(csh, seqs, device=DEV)
     torch.cuda.synchronize()
     # calibration parity on the same sequences
-    cal = R.Calibrator(R.make_shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt))
+    cal = R.Calibrator(R.make_shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode))
     for cx, cm in seqs:
         cal.accumulate(np_sym(cx, w.sym_fmt), np_mu(cm, w.mu_fmt), nthreads=16)
     rsigma, rhist = cal.finalize()
@@ -42,7 +43,7 @@ def test_full_size_roundtrip_and_sampled_oracle_parity(name):
     del seqs
 
     x, mu = synth.generate(w, device=DEV)
-    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
     buf = skv.Buffers(sh, device=DEV)
     buf.encode(x, mu, sigma, hist)
     out = torch.empty_like(x)
@@ -57,7 +58,8 @@ def test_full_size_roundtrip_and_sampled_oracle_parity(name):
 
     # sampled chunks against the oracle, one by one
     model = R.Model(w.sym_fmt, rhist)
-    rsh = R.make_shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt)
+    rsh = R.make_shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
+    per_ch = R.OCT_STRIDE if w.sigma_mode == R.SIGMA_OCTAVE else 1
     nc = len(offs) - 1
     ntb = (w.tokens + 255) // 256
     rng = np.random.default_rng(sum(map(ord, name)))
@@ -70,7 +72,7 @@ def test_full_size_roundtrip_and_sampled_oracle_parity(name):
         t1 = min(w.tokens, t0 + 256)
         xc = np_sym(xr[row, t0:t1], w.sym_fmt).ravel()
         mc = np_mu(mr[row, t0:t1], w.mu_fmt).ravel()
-        sc = np.ascontiguousarray(rsigma[row * w.head_dim:(row + 1) * w.head_dim])
+        sc = np.ascontiguousarray(rsigma[row * w.head_dim * per_ch:(row + 1) * w.head_dim * per_ch])
         want = model.encode_chunk(rsh, c, xc, mc, sc)
         got = buf.bits[int(offs[c]):int(offs[c + 1])].cpu().numpy()
         assert np.array_equal(got, want), f"chunk {c} differs from the oracle"

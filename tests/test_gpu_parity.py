@@ -1,6 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs.  Bit-exact: stream bytes, offsets, decoded symbols,
 calibrated sigma and histogram."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -18,14 +20,23 @@ def _built():
     ensure_built()
 
 
+def _workload(name):
+    """A named workload; "<name>_oct" not in the table: that workload coded in octave mode."""
+    if name in synth.WORKLOADS:
+        return synth.WORKLOADS[name]
+    assert name.endswith("_oct")
+    return dataclasses.replace(synth.WORKLOADS[name[:-4]], name=name, sigma_mode=1)
+
+
 def _reduced(name, layers=2, tokens=600, calib_seqs=2):
-    w = synth.WORKLOADS[name]
-    if name != "tiny_bf16":
+    w = _workload(name)
+    if not name.startswith("tiny_bf16"):
         w = w.with_tokens(tokens, layers=layers)
     return w, min(calib_seqs, w.calib_seqs)
 
 
-CASES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k", "qwen3_32b_bf16_fp8res"]
+CASES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k", "qwen3_32b_bf16_fp8res",
+         "qwen3_32b_bf16_fp8res_oct", "qwen3_0.6b_e4m3_oct", "tiny_bf16_oct"]
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -118,6 +129,31 @@ def test_ragged_shapes(tokens, head_dim, sym):
     rng = np.random.default_rng(tokens + head_dim)
     x, mu = synth.generate(w)
     sigma = (0.02 * np.exp(rng.standard_normal(w.n_channels))).astype(np.float32)
+    hist = rng.integers(0, 9, 65536 if sym == 0 else 256).astype(np.uint64)
+    sh, rsh = shapes(w)
+    bits, offs, out, st_e, st_d = gpu_roundtrip(sh, x.to(DEV), mu.to(DEV), torch.from_numpy(sigma).to(DEV),
+                                                torch.from_numpy(hist.view(np.int64)).to(DEV))
+    assert st_e == skv.OK and st_d == skv.OK
+    rbits, roffs = R.Model(sym, hist).encode(rsh, np_sym(x, sym), np_mu(mu, 0), sigma)
+    np.testing.assert_array_equal(offs, roffs)
+    np.testing.assert_array_equal(bits, rbits)
+    assert torch.equal(out.cpu(), x)
+
+
+@pytest.mark.parametrize("tokens,head_dim,sym", [(3, 128, 0), (300, 64, 1), (257, 8, 0), (40, 512, 1), (600, 256, 0)])
+def test_ragged_shapes_octave_mode(tokens, head_dim, sym):
+    """Octave mode on every scale period (head_dim 8 .. 512) and ragged chunks,
+    with a random table (zero, tiny and large sigmas) and non-finite means."""
+    w = synth.Workload("ragged_oct", 1, 2, 3, head_dim, tokens, sym, 0, 0.02, 1, 64, "mixture", 1)
+    rng = np.random.default_rng(tokens + head_dim + 7)
+    x, mu = synth.generate(w)
+    mu = mu.clone()
+    mu.view(-1)[::97] = 0x7FC0   # NaN means read as 0
+    mu.view(-1)[::89] = -128     # 0xFF80 = -inf
+    table = np.exp(rng.uniform(-9, 1, (w.n_channels, R.OCT_STRIDE))).astype(np.float32)
+    table[::5, 0] = 0.0
+    table[::7, 3] = 0.0
+    sigma = np.ascontiguousarray(table.reshape(-1))
     hist = rng.integers(0, 9, 65536 if sym == 0 else 256).astype(np.uint64)
     sh, rsh = shapes(w)
     bits, offs, out, st_e, st_d = gpu_roundtrip(sh, x.to(DEV), mu.to(DEV), torch.from_numpy(sigma).to(DEV),
