@@ -451,13 +451,15 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     // a divisor of kBatch
     float s[PER], sinv[PER];
     int32_t er[PER];  // octave mode: the channels' octave references
-    uint32_t cb[PER]; // octave mode: the channels' first table entries
+    uint32_t cb[PER]; // octave mode: the channels' column in the row's [octave][d] scale table
+    const float2 *srow = a.scale + (OCT ? row * kOctaves * g.D : 0);
+    const uint32_t lgD = (uint32_t)__builtin_ctz(D);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int64_t ch = row * g.D + ((lane + kLanes * j) & (D - 1));
       if (OCT) {
         er[j] = a.eref[ch];
-        cb[j] = (uint32_t)(ch * kOctaves);
+        cb[j] = (uint32_t)((lane + kLanes * j) & (D - 1));
       } else {
         const float2 sc = a.scale[ch];
         s[j] = sc.x;
@@ -493,7 +495,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       float2 sb[kBatch];
       if (OCT) {
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) sb[j] = a.scale[cb[j % PER] + octave_of(cur.get(j), er[j % PER])];
+        for (int j = 0; j < kBatch; ++j) sb[j] = srow[(octave_of(cur.get(j), er[j % PER]) << lgD) + cb[j % PER]];
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
@@ -522,7 +524,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
             b0 = cb[q];
           }
         }
-        const float2 sc = a.scale[b0 + octave_of(m, e)];
+        const float2 sc = srow[(octave_of(m, e) << lgD) + b0];
         sj = sc.x;
         sij = sc.y;
       } else {

@@ -403,13 +403,15 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     // two up to 512 that repeats with period PER = max(2, D / 64), which divides kBatch
     float s[PER];
     int32_t er[PER];  // octave mode: the channels' octave references
-    uint32_t cb[PER]; // octave mode: the channels' first table entries
+    uint32_t cb[PER]; // octave mode: the channels' column in the row's [octave][d] scale table
+    const float2 *srow = a.scale + (OCT ? row * kOctaves * g.D : 0);
+    const uint32_t lgD = (uint32_t)__builtin_ctz(D);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int64_t ch = row * g.D + ((lane + kLanes * j) & (D - 1));
       if (OCT) {
         er[j] = a.eref[ch];
-        cb[j] = (uint32_t)(ch * kOctaves);
+        cb[j] = (uint32_t)((lane + kLanes * j) & (D - 1));
       } else {
         s[j] = a.scale[ch].x;
       }
@@ -428,10 +430,17 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;  // this lane's symbols
     const int nfull = nsc / kStep;                                         // batches every lane fills
     Batch<SYM, MU> cur, nxt;
+    // octave mode: a batch's scales depend on its means; they are read half a
+    // batch ahead, once the next batch's means have arrived
+    float sb[kBatch], sbn[kBatch];
     if (nfull > 0) {
       cur.load_full(a, base + lane);
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
+      if (OCT) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) sb[j] = srow[(octave_of(cur.mu(j), er[j % PER]) << lgD) + cb[j % PER]].x;
+      }
     }
     for (int b = 0; b < nfull; ++b) {
       // this batch's symbols and means were loaded one batch ago; wait for
@@ -439,19 +448,21 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
       if (b + 1 < nfull) nxt.load_full(a, base + lane + (int64_t)(b + 1) * kStep);  // in flight meanwhile
-      // octave mode: the batch's scales, read at its start (the means are here)
-      float sb[kBatch];
-      if (OCT) {
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) sb[j] = a.scale[cb[j % PER] + octave_of(cur.mu(j), er[j % PER])].x;
-      }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
+        if (OCT && j == kBatch / 2 && b + 1 < nfull) {
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) sbn[q] = srow[(octave_of(nxt.mu(q), er[q % PER]) << lgD) + cb[q % PER]].x;
+        }
         uint32_t c, f;
         model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), OCT ? sb[j] : s[j % PER], c, f);
         cod.encode(c, f);
       }
       cur = nxt;
+      if (OCT) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) sb[j] = sbn[j];
+      }
     }
     // the last, partial batch of a short chunk: symbol by symbol
     for (int k = nfull * kBatch; k < nk; ++k) {
@@ -468,7 +479,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
             e = er[q];
             b0 = cb[q];
           }
-        sj = a.scale[b0 + octave_of(cur.mu(0), e)].x;
+        sj = srow[(octave_of(cur.mu(0), e) << lgD) + b0].x;
       } else {
         sj = s[0];
 #pragma unroll

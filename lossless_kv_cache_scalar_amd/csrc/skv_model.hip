@@ -214,12 +214,15 @@ __global__ void k_scale(const float *__restrict__ sigma, float2 *__restrict__ sc
   scale[i] = make_float2(sc, __builtin_amdgcn_rcpf(sc));
 }
 
-// Octave mode: per channel c (one thread), eref = E(max(sigma_c, 2^-100)) + 1
-// and the (s, ~1/s) of its eight octave sigmas, from the SKV_OCT_STRIDE table.
+// Octave mode: per channel c = row * D + d (one thread), eref = E(max(sigma_c,
+// 2^-100)) + 1 and the (s, ~1/s) of its eight octave sigmas, from the
+// SKV_OCT_STRIDE table, stored at [row][octave][d] so that the lanes of a wave
+// (consecutive channels of one row) read side by side.
 __global__ void k_scale_oct(const float *__restrict__ table, float2 *__restrict__ scale, int32_t *__restrict__ eref,
-                            int64_t nch, int32_t *status) {
+                            int64_t nch, int64_t D, int32_t *status) {
   int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= nch) return;
+  const int64_t row = c / D, d = c - row * D;
   const float *t = table + c * SKV_OCT_STRIDE;
   bool bad = false;
   float sg0 = t[0];
@@ -237,7 +240,7 @@ __global__ void k_scale_oct(const float *__restrict__ table, float2 *__restrict_
     }
     const float sp = sg > 0x1p-100f ? sg : 0x1p-100f;
     const float sc = (float)(64.0 / (double)sp);
-    scale[c * kOctaves + j] = make_float2(sc, __builtin_amdgcn_rcpf(sc));
+    scale[(row * kOctaves + j) * D + d] = make_float2(sc, __builtin_amdgcn_rcpf(sc));
   }
   if (bad) set_status(status, SKV_ERR_ARG);
 }
@@ -265,7 +268,7 @@ hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, 
   int64_t nch = g.rows * g.D;
   if (g.octave)
     hipLaunchKernelGGL(k_scale_oct, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, sigma, ws.scale, ws.eref,
-                       nch, status);
+                       nch, g.D, status);
   else
     hipLaunchKernelGGL(k_scale, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, st, sigma, ws.scale, nch, status);
   timing_mark(kTimeModel, true, st);
