@@ -59,22 +59,27 @@ struct LaneReader {
   uint32_t csize;        // chunk bytes (a multiple of 4, >= 192)
   uint32_t m;            // interleaved words per lane
   uint32_t tail, len;    // chunk offset of the lane's tail, lane length
-  uint32_t ip;           // chunk offset of interleaved word w of the lane
+  uint32_t ip0;          // chunk offset of the lane's interleaved word 0 (word w: ip0 + 256 w)
   uint32_t w, plo, phi;
   uint64_t ib;  // next bits, left-aligned
   int nib;      // valid bits in ib
 
+  bool fast;    // wave-uniform: at the last issue no lane was past its interleaved words
+
   __device__ __forceinline__ void issue() {
     const bool tl = w >= m;
-    uint32_t a0 = ip;  // an interleaved word never lies past the lane's end
-    if (__builtin_expect(__any(tl), 0)) {
+    fast = !__any(tl);
+    uint32_t a0 = ip0 + (w << 8);  // an interleaved word never lies past the lane's end
+    if (__builtin_expect(!fast, 0)) {
       if (tl) {
         a0 = (tail + 4u * (w - m)) & ~3u;
         if (4u * w >= len) a0 = 0u;  // nothing left: any dword of the chunk, masked off below
       }
     }
+    // one load for both cases: separate loads per branch would be merged
+    // with a copy that waits for the data
     plo = *reinterpret_cast<const uint32_t *>(chunk + a0);
-    if (__builtin_expect(__any(tl), 0)) {
+    if (__builtin_expect(!fast, 0)) {
       uint32_t a1 = a0 + 4u;
       if (a1 >= csize) a1 = a0;
       phi = *reinterpret_cast<const uint32_t *>(chunk + a1);
@@ -82,10 +87,11 @@ struct LaneReader {
   }
   // renormalisation bytes taken so far (after the 6 priming bytes)
   __device__ __forceinline__ uint32_t renorm_bytes() const { return (32u * w - (uint32_t)nib) / 8u - 6u; }
+  // word w of the lane, from the loads of the last issue (made for this w)
   __device__ __forceinline__ uint32_t word() const {
-    if (__builtin_expect(w < m, 1)) return __builtin_bswap32(plo);
-    const uint32_t sh = 8u * (tail & 3u);
-    uint32_t v = __builtin_bswap32((uint32_t)((((uint64_t)phi << 32) | plo) >> sh));
+    if (__builtin_expect(fast, 1) || w < m) return __builtin_bswap32(plo);
+    // bytes tail mod 4 .. of phi:plo (two separate registers: no pair to merge)
+    uint32_t v = __builtin_bswap32(__builtin_amdgcn_alignbyte(phi, plo, tail & 3u));
     const int valid = (int)len - 4 * (int)w;
     if (valid <= 0) return 0u;
     if (valid < 4) v &= ~(0xFFFFFFFFu >> (8 * valid));
@@ -93,16 +99,14 @@ struct LaneReader {
   }
   __device__ __forceinline__ void init(uint32_t lane) {
     w = 0;
-    ip = kHeaderBytes + 4u * lane;
+    ip0 = kHeaderBytes + 4u * lane;
     issue();
     ib = (uint64_t)word() << 32;
     w = 1;
-    ip += 4u * kLanes;
     issue();
     ib |= word();
     nib = 64;
     w = 2;
-    ip += 4u * kLanes;
     issue();
   }
   // n in {0, 8, 16, 24}
@@ -111,7 +115,6 @@ struct LaneReader {
       ib |= (uint64_t)word() << (32 - nib);
       nib += 32;
       ++w;
-      ip += 4u * kLanes;
     }
     const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)(ib >> 32), (0u - n) & 31u, n);
     ib <<= n;
@@ -125,7 +128,6 @@ struct LaneReader {
       ib |= (uint64_t)word() << (32 - nib);
       nib += 32;
       ++w;
-      ip += 4u * kLanes;
     }
     const uint64_t lo = (((uint64_t)(uint32_t)x << 32) | (uint32_t)(ib >> 32)) << n;
     const uint64_t r = ((x << n) & 0xFFFFFFFF00000000ull) | (lo >> 32);
@@ -163,11 +165,12 @@ __device__ __forceinline__ uint32_t a_guess(const ModelTabs &t, uint32_t k) {
 
 // The symbol whose bin holds the value where the Gaussian pair's CDF reaches
 // t - A(k): the inverse table gives the knot coordinate, mu + u sigma / 64 the
-// value, and rounding to the symbol format the guess.
+// value, and rounding to the symbol format the guess.  ts is t in steps of the
+// inverse table (kNInv / MG counts per step).
 template <int SYM, int TAB>
-__device__ __forceinline__ uint32_t guess_symbol(const ModelTabs &t, const float2 *uinv, float tq, uint32_t k,
+__device__ __forceinline__ uint32_t guess_symbol(const ModelTabs &t, const float2 *uinv, float ts, uint32_t k,
                                                  float inv_step, float sinv, float m) {
-  float mf = (tq - (float)a_guess<SYM, TAB>(t, k)) * inv_step;
+  float mf = __builtin_fmaf((float)a_guess<SYM, TAB>(t, k), -inv_step, ts);
   mf = __builtin_fminf(__builtin_fmaxf(mf, 0.0f), (float)kNInv - 0.5f);
   const int ii = (int)mf;  // mf >= 0: truncation is the floor
   const float2 ud = uinv[ii];
@@ -247,7 +250,7 @@ struct MuBatch {
     for (int j = 0; j < kBatch; ++j) v[j] = one(mu, i0 + kLanes * j);
   }
   __device__ __forceinline__ float get(int j) const {
-    return MU == SKV_MU_BF16 ? mu_from_bf16(v[j]) : mu_from_f32(__uint_as_float(v[j]));
+    return mu_finite_wave(MU == SKV_MU_BF16 ? __uint_as_float(v[j] << 16) : __uint_as_float(v[j]));
   }
 };
 
@@ -255,7 +258,7 @@ struct MuBatch {
 // lane of the wave is active): one secant step in rank space from the guess's
 // exact counts, then galloping and bisection.
 template <int SYM, int TAB>
-__device__ __forceinline__ void resolve_alone(const ModelTabs &t, bool ok, bool below, float tq, uint32_t &gs,
+__device__ __forceinline__ void resolve_alone(const ModelTabs &t, bool ok, bool below, uint32_t &gs,
                                               uint32_t &clo, uint32_t &chi, float m, float sj, uint64_t d, uint32_t r,
                                               uint64_t &dd, uint64_t &pf, bool &corrupt) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
@@ -264,6 +267,7 @@ __device__ __forceinline__ void resolve_alone(const ModelTabs &t, bool ok, bool 
   if (!ok) {
     // one secant step in rank space on the guess's exact counts
     const uint32_t kg = BF ? rank_bf16(gs) : rank_e4m3(gs);
+    const float tq = (float)(uint32_t)(d >> 16) * (65536.0f * __builtin_amdgcn_rcpf((float)(r << up)));
     const float st = (tq - (float)clo) * __builtin_amdgcn_rcpf((float)(chi - clo));
     int step = (int)__builtin_floorf(__builtin_fminf(__builtin_fmaxf(st, -70000.0f), 70000.0f));
     step = below ? min(step, -1) : max(step, 1);
@@ -374,13 +378,14 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   // ---- guess: invert the Gaussian pair's CDF at t - A(k), first with k the
   // rank of mu, then with k the rank of that first guess (the one-count floor
   // makes A(k) grow by one per rank, which matters near zero)
-  const float tq = (float)(uint32_t)(d >> 16) * (65536.0f * __builtin_amdgcn_rcpf((float)(r << up)));
+  // t = d / r in units of the inverse table's step
+  const float ts = (float)(uint32_t)(d >> 16) * (a.inv_step * 65536.0f * __builtin_amdgcn_rcpf((float)(r << up)));
   // (any start serves: a non-finite bf16 mean starts from its own pattern)
   uint32_t kmu;
   if (BF) kmu = tix_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : mraw);
   else kmu = rank_e4m3(e4m3_guess(m));
-  uint32_t gs = guess_symbol<SYM, TAB>(t, uinv, tq, kmu, a.inv_step, sinvj, m);
-  gs = guess_symbol<SYM, TAB>(t, uinv, tq, BF ? tix_bf16(gs) : rank_e4m3(gs), a.inv_step, sinvj, m);
+  uint32_t gs = guess_symbol<SYM, TAB>(t, uinv, ts, kmu, a.inv_step, sinvj, m);
+  gs = guess_symbol<SYM, TAB>(t, uinv, ts, BF ? tix_bf16(gs) : rank_e4m3(gs), a.inv_step, sinvj, m);
   // ---- verify exactly
   uint32_t clo, chi;
   uint64_t dd, pf;
@@ -388,7 +393,7 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   const bool ok = verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below);
   if (__builtin_expect(__any(!ok), 0)) {
     if (__ballot(1) == ~0ull) resolve_misses<SYM, TAB>(t, !ok, below, gs, clo, chi, m, sj, d, r, dd, pf, corrupt);
-    else resolve_alone<SYM, TAB>(t, ok, below, tq, gs, clo, chi, m, sj, d, r, dd, pf, corrupt);
+    else resolve_alone<SYM, TAB>(t, ok, below, gs, clo, chi, m, sj, d, r, dd, pf, corrupt);
   }
   // ---- update and renormalise
   const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & 24u;  // pf >= r >= 2^16: clz & ~7

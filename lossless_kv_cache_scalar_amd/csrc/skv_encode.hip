@@ -226,7 +226,11 @@ struct LaneCoder {
     const uint64_t Xn = Xo + mul24(r, c);
     const bool carry = Xn < Xo;
     X = Xn;
-    const uint64_t rg = mul24(r, f);
+    // r * f as the two 24-bit multiplies, written out: r also feeds the 32-bit
+    // multiply-add above, and the compiler would mask it to 24 bits here
+    uint32_t rlo, rhi;
+    asm("v_mul_u32_u24 %0, %2, %3\n\tv_mul_hi_u32_u24 %1, %2, %3" : "=&v"(rlo), "=v"(rhi) : "v"(r), "v"(f));
+    const uint64_t rg = ((uint64_t)rhi << 32) | rlo;
     // bytes to shift, x8: rg >= 2^16 (f >= 1) makes this clz & ~7; the mask
     // bounds it by 24 whatever rg is, so a lane never emits more than 3 bytes
     // per symbol and never outgrows its slot
@@ -272,7 +276,7 @@ struct Batch {
     for (int j = 0; j < kBatch; ++j) one(a, i0 + (int64_t)kLanes * j, j);
   }
   __device__ __forceinline__ float mu(int j) const {
-    return MU == SKV_MU_BF16 ? mu_from_bf16(ms[j]) : mu_from_f32(__uint_as_float(ms[j]));
+    return mu_finite_wave(MU == SKV_MU_BF16 ? __uint_as_float(ms[j] << 16) : __uint_as_float(ms[j]));
   }
 };
 
@@ -314,7 +318,8 @@ __device__ __forceinline__ void model_common(const EncArgs &a, const EncTables &
     // while the Gaussian pair is evaluated
     uint32_t alo, ahi;
     a_pair_bf16<FAST>(a, t, b, alo, ahi);
-    const uint32_t eA = (b << 16) | 0x8000u;
+    uint32_t eA;  // (b << 16) | 0x8000 as one shift-or
+    asm("v_lshl_or_b32 %0, %1, 16, %2" : "=v"(eA) : "v"(b), "s"(0x8000u));
     const uint32_t eB = eA - 0x10000u;
     const uint32_t cA = cg_eval(t.kn, u_of(__uint_as_float(eA), m, sj));
     const uint32_t cB = cg_eval(t.kn, u_of(__uint_as_float(eB), m, sj));

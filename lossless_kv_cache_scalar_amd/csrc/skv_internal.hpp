@@ -128,6 +128,13 @@ __device__ __forceinline__ float mu_from_bf16(uint32_t bits16) {
   return __builtin_isfinite(f) ? f : 0.0f;
 }
 __device__ __forceinline__ float mu_from_f32(float f) { return __builtin_isfinite(f) ? f : 0.0f; }
+// the same rule where a whole wave reads means: one class test per lane, and the
+// select only on the rare step where some lane's mean is not finite
+__device__ __forceinline__ float mu_finite_wave(float f) {
+  const bool bad = !__builtin_isfinite(f);
+  if (__builtin_expect(__any(bad), 0)) f = bad ? 0.0f : f;
+  return f;
+}
 
 // knot coordinate u = RN(RN(e - mu) * s); the build turns contraction off
 __device__ __forceinline__ float u_of(float e, float mu, float s) {

@@ -50,7 +50,8 @@ template <int TAB>
 __device__ __forceinline__ uint32_t a_one(const ModelTabs &t, uint32_t ti) {
   if (TAB == kTabGlobal) return t.ptab[ti ^ 0x8000u];
   const uint32_t w = ti >> 6;
-  return t.ab[w] + t.a16[ti + w];
+  // entry ti + w, addressed in bytes as one add-and-shift
+  return t.ab[w] + *reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(t.a16) + ((ti + w) << 1));
 }
 
 // cum_lo and cum_hi of symbol b in model units (bf16: total 2^24, e4m3: 2^16)
@@ -67,7 +68,8 @@ __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float
     // count is the min of the two.  +-0, +-inf and NaN take the general edges
     // (the counts are complete before that rare branch, which redoes them, so
     // the table reads and their sums stay in one block).
-    const uint32_t eA = (b << 16) | 0x8000u;
+    uint32_t eA;  // (b << 16) | 0x8000 as one shift-or
+    asm("v_lshl_or_b32 %0, %1, 16, %2" : "=v"(eA) : "v"(b), "s"(0x8000u));
     const uint32_t eB = eA - 0x10000u;
     const uint32_t cA = cg_eval(t.kn, u_of(__uint_as_float(eA), m, s));
     const uint32_t cB = cg_eval(t.kn, u_of(__uint_as_float(eB), m, s));
