@@ -146,20 +146,21 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return v;
 }
 
-// e4m3 pattern near e (round to nearest, saturating): a first guess only
-__device__ __forceinline__ uint32_t e4m3_guess(float e) {
-  const uint32_t sgn = (__float_as_uint(e) >> 24) & 0x80u;
-  const float a = __builtin_fminf(__builtin_fabsf(e), 448.0f);
-  uint32_t code;
-  if (a >= 0x1p-6f) code = ((__float_as_uint(a) + 0x7FFFFu) >> 20) - (120u << 3);
-  else code = (uint32_t)__builtin_rintf(a * 512.0f);
-  return sgn | min(code, 0x7Eu);
+// e4m3 pattern of e, rounded to nearest even with saturation: the hardware
+// conversion (OCP e4m3, which gives NaN beyond 464), on e clamped to +-448.
+// The instruction writes the low 16 bits only: the word starts at zero, and
+// the second operand 0.0 converts to a zero byte.
+__device__ __forceinline__ uint32_t e4m3_rne_bits(float e) {
+  uint32_t v = 0;
+  const float c = __builtin_amdgcn_fmed3f(e, -448.0f, 448.0f);
+  asm("v_cvt_pk_fp8_f32 %0, %1, 0" : "+v"(v) : "v"(c));
+  return v;
 }
 
-// A(k) for a guess; k is the rank (e4m3) or the table index tix_bf16 (bf16)
+// A(k) for a guess; k is the table index (tix_bf16 or tix_e4m3)
 template <int SYM, int TAB>
 __device__ __forceinline__ uint32_t a_guess(const ModelTabs &t, uint32_t k) {
-  if (SYM != SKV_SYM_BF16) return t.ab[k];
+  if (SYM != SKV_SYM_BF16) return t.ab[2u * k];
   return a_one<TAB>(t, k);
 }
 
@@ -176,7 +177,7 @@ __device__ __forceinline__ uint32_t guess_symbol(const ModelTabs &t, const float
   const float2 ud = uinv[ii];
   const float uu = __builtin_fmaf(__builtin_amdgcn_fractf(mf), ud.y, ud.x);
   const float e = __builtin_fmaf(uu, sinv, m);
-  return SYM == SKV_SYM_BF16 ? bf16_rne_bits(e) : e4m3_guess(e);
+  return SYM == SKV_SYM_BF16 ? bf16_rne_bits(e) : e4m3_rne_bits(e);
 }
 
 // The exact rank: the largest k with r * (cum(k) << up) <= d.  Known so far:
@@ -383,9 +384,9 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   // (any start serves: a non-finite bf16 mean starts from its own pattern)
   uint32_t kmu;
   if (BF) kmu = tix_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : mraw);
-  else kmu = rank_e4m3(e4m3_guess(m));
+  else kmu = tix_e4m3(e4m3_rne_bits(m));
   uint32_t gs = guess_symbol<SYM, TAB>(t, uinv, ts, kmu, a.inv_step, sinvj, m);
-  gs = guess_symbol<SYM, TAB>(t, uinv, ts, BF ? tix_bf16(gs) : rank_e4m3(gs), a.inv_step, sinvj, m);
+  gs = guess_symbol<SYM, TAB>(t, uinv, ts, BF ? tix_bf16(gs) : tix_e4m3(gs), a.inv_step, sinvj, m);
   // ---- verify exactly
   uint32_t clo, chi;
   uint64_t dd, pf;
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   __shared__ float2 s_kn[kNKnot];
   __shared__ float2 s_ui[kNInv + 1];
   __shared__ uint32_t s_a16w[BF ? kNWin * kWinEntries / 2 : 1];
-  __shared__ uint32_t s_ab[BF ? kNWin + 1 : 257];
+  __shared__ __align__(8) uint32_t s_ab[BF ? kNWin + 1 : 512];
   __shared__ float2 s_et[BF ? 1 : 256];
 
   const bool win = BF ? *a.aflag != 0 : true;
@@ -573,7 +574,8 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
       for (int i = threadIdx.x; i <= kNWin; i += kDecBlock) s_ab[i] = a.abase[i];
     }
   } else {
-    for (int i = threadIdx.x; i < 257; i += kDecBlock) s_ab[i] = a.ptab[i];
+    // (A(k), A(k + 1)) side by side at table index k ^ 0x80
+    for (int i = threadIdx.x; i < 512; i += kDecBlock) s_ab[i] = a.ptab[((uint32_t)i >> 1 ^ 0x80u) + (i & 1)];
     for (int i = threadIdx.x; i < 256; i += kDecBlock) s_et[i] = a.etab[i];
   }
   __syncthreads();

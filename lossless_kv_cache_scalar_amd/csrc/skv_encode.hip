@@ -328,9 +328,9 @@ __device__ __forceinline__ void model_common(const EncArgs &a, const EncTables &
     f = ahi + max(cA, cB) - c;
   } else {
     const float2 e = t.et[b];
-    const uint32_t k = rank_e4m3(b);
-    const uint32_t lo = t.ab[k] + cg_eval(t.kn, u_of(e.x, m, sj));
-    const uint32_t hi = t.ab[k + 1] + cg_eval(t.kn, u_of(e.y, m, sj));
+    const uint2 p = reinterpret_cast<const uint2 *>(t.ab)[tix_e4m3(b)];  // (A(k), A(k + 1))
+    const uint32_t lo = p.x + cg_eval(t.kn, u_of(e.x, m, sj));
+    const uint32_t hi = p.y + cg_eval(t.kn, u_of(e.y, m, sj));
     c = lo << 8;
     f = (hi - lo) << 8;
     special = false;
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   __shared__ float2 s_kn[kNKnot];
   __shared__ uint32_t s_a16w[BF ? kNWin * kWinEntries / 2 : 1];
-  __shared__ uint32_t s_ab[BF ? kNWin + 1 : 257];
+  __shared__ __align__(8) uint32_t s_ab[BF ? kNWin + 1 : 512];
   __shared__ float2 s_et[BF ? 1 : 256];
 
   const bool fast = BF ? *a.aflag != 0 : true;  // windowed p_hat table usable
@@ -546,7 +546,8 @@ __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
       for (int i = threadIdx.x; i <= kNWin; i += kEncBlock) s_ab[i] = a.abase[i];
     }
   } else {
-    for (int i = threadIdx.x; i < 257; i += kEncBlock) s_ab[i] = a.ptab[i];
+    // (A(k), A(k + 1)) side by side at table index k ^ 0x80
+    for (int i = threadIdx.x; i < 512; i += kEncBlock) s_ab[i] = a.ptab[((uint32_t)i >> 1 ^ 0x80u) + (i & 1)];
     for (int i = threadIdx.x; i < 256; i += kEncBlock) s_et[i] = a.etab[i];
   }
   __syncthreads();

@@ -91,6 +91,13 @@ __device__ __forceinline__ uint32_t tix_bf16(uint32_t b) {
   return t;
 }
 __device__ __forceinline__ uint32_t rank_e4m3(uint32_t b) { return b ^ ((b & 0x80u) ? 0xFFu : 0x80u); }
+// e4m3 table index of pattern b < 256: rank ^ 0x80 = b ^ (b >= 0x80 ? 0x7F : 0),
+// the same two instructions as tix_bf16 on 8 bits
+__device__ __forceinline__ uint32_t tix_e4m3(uint32_t b) {
+  uint32_t t;
+  asm("v_bfe_i32 %0, %1, 7, 1\n\tv_bitop3_b32 %0, %0, %1, %2 bitop3:0x6c" : "=&v"(t) : "v"(b), "s"(0x7Fu));
+  return t;
+}
 __device__ __forceinline__ uint32_t unrank_e4m3(uint32_t k) { return k ^ ((k & 0x80u) ? 0x80u : 0xFFu); }
 
 // bf16 bin of pattern b: the fp32 values that round (nearest-even) to b.

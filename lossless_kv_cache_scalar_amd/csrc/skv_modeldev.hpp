@@ -24,7 +24,7 @@ enum { kTabGlobal = 0,   // A from global memory only (the 16-bit window image d
 struct ModelTabs {
   const float2 *kn;      // LDS: knots (K_j, D_j)
   const uint16_t *a16;   // LDS: window image (bf16), window slots as tix_bf16 orders them
-  const uint32_t *ab;    // LDS: window bases (bf16); e4m3: the full table A in rank order
+  const uint32_t *ab;    // LDS: window bases (bf16); e4m3: (A(k), A(k + 1)) at 2 tix_e4m3, 2 tix_e4m3 + 1
   const uint32_t *ptab;  // global: full table A in rank order
   const float2 *et;      // LDS: e4m3 bins
 };
@@ -87,9 +87,9 @@ __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float
     }
   } else {
     const float2 e = t.et[b];
-    const uint32_t k = rank_e4m3(b);
-    clo = t.ab[k] + cg_eval(t.kn, u_of(e.x, m, s));
-    chi = t.ab[k + 1] + cg_eval(t.kn, u_of(e.y, m, s));
+    const uint2 p = reinterpret_cast<const uint2 *>(t.ab)[tix_e4m3(b)];
+    clo = p.x + cg_eval(t.kn, u_of(e.x, m, s));
+    chi = p.y + cg_eval(t.kn, u_of(e.y, m, s));
   }
 }
 
@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t cum_rank(const ModelTabs &t, uint32_t k, flo
     return a_one<TAB>(t, k ^ 0x8000u) + cg_eval(t.kn, u_of(__uint_as_float(e), m, s));
   } else {
     if (k >= 256u) return 1u << 16;
-    return t.ab[k] + cg_eval(t.kn, u_of(t.et[unrank_e4m3(k)].x, m, s));
+    return t.ab[2u * (k ^ 0x80u)] + cg_eval(t.kn, u_of(t.et[unrank_e4m3(k)].x, m, s));
   }
 }
 
