@@ -50,15 +50,15 @@ def csrc_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources."""
+    were taken on the current kernel sources and on this workload."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("csrc_hash") != csrc_hash():
+    if rec.get("csrc_hash") != csrc_hash() or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -166,7 +166,7 @@ def main():
     dec_hbm = moved / dec_ms / 1e6
     kern = "k_decode" if kern_avg["k_decode"] >= kern_avg["k_encode"] else "k_encode"
     kms = kern_avg[kern]
-    traffic = measured_traffic(kern)
+    traffic = measured_traffic(kern, w.name)
 
     result = {
         "metric": METRIC,
