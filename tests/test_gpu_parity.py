@@ -102,6 +102,9 @@ def test_every_e4m3_pattern(mu_fmt):
     vals = np.nan_to_num(np.array([R.value(1, v) for v in range(256)]), nan=0.0)
     muf = (vals[x] + rng.standard_normal(x.shape) * np.exp(rng.uniform(-6, 6, x.shape))).astype(np.float32)
     muf.reshape(-1)[::37] = np.nan
+    muf.reshape(-1)[::41] = np.inf     # read as 0
+    muf.reshape(-1)[::43] = -1e30      # far beyond +-448: bf16 keeps it, the guesses clamp
+    muf.reshape(-1)[::47] = 600.0
     if mu_fmt == 0:
         mu = torch.from_numpy(muf).to(torch.bfloat16).view(torch.int16)
         mun = mu.numpy().view(np.uint16)
