@@ -460,6 +460,9 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     uint32_t cb[PER]; // octave mode: the channels' column in the row's [octave][d] scale table
     const float2 *srow = a.scale + (OCT ? row * kOctaves * g.D : 0);
     const uint32_t lgD = (uint32_t)__builtin_ctz(D);
+    // octave mode, full batches: the row's table from scalar registers, a
+    // scale pair at byte offset (octave << (lgD + 3)) + 8 d
+    const char *srow_b = reinterpret_cast<const char *>(OCT ? wave_uniform(srow) : srow);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int64_t ch = row * g.D + ((lane + kLanes * j) & (D - 1));
@@ -496,17 +499,25 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       // per batch, and not inside the symbols
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.v[j]));
-      if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
       // octave mode: the batch's scales, read at its start (the means are here)
+      // and before the next batch's loads: loads complete in order, so the
+      // first symbol's wait for them leaves the next batch in flight
       float2 sb[kBatch];
+      float mj[kBatch];  // (octave mode: the means, converted once)
       if (OCT) {
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) sb[j] = srow[(octave_of(cur.get(j), er[j % PER]) << lgD) + cb[j % PER]];
+        for (int j = 0; j < kBatch; ++j) {
+          mj[j] = cur.get(j);
+          sb[j] = *reinterpret_cast<const float2 *>(srow_b + ((octave_of(mj[j], er[j % PER]) << (lgD + 3)) +
+                                                             (cb[j % PER] << 3)));
+        }
       }
+      if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, cur.get(j), cur.v[j],
-                                                        OCT ? sb[j].x : s[j % PER], OCT ? sb[j].y : sinv[j % PER]);
+        const uint32_t gs =
+            decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, OCT ? mj[j] : cur.get(j), cur.v[j],
+                                        OCT ? sb[j].x : s[j % PER], OCT ? sb[j].y : sinv[j % PER]);
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
         else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;

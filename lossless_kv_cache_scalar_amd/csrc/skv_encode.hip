@@ -411,6 +411,12 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     uint32_t cb[PER]; // octave mode: the channels' column in the row's [octave][d] scale table
     const float2 *srow = a.scale + (OCT ? row * kOctaves * g.D : 0);
     const uint32_t lgD = (uint32_t)__builtin_ctz(D);
+    // octave mode, full batches: the row's table from scalar registers, a
+    // scale at byte offset (octave << (lgD + 3)) + 8 d
+    const char *srow_b = reinterpret_cast<const char *>(OCT ? wave_uniform(srow) : srow);
+    auto scale_at = [&](float m, int j) {
+      return *reinterpret_cast<const float *>(srow_b + ((octave_of(m, er[j % PER]) << (lgD + 3)) + (cb[j % PER] << 3)));
+    };
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int64_t ch = row * g.D + ((lane + kLanes * j) & (D - 1));
@@ -444,7 +450,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
       if (OCT) {
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) sb[j] = srow[(octave_of(cur.mu(j), er[j % PER]) << lgD) + cb[j % PER]].x;
+        for (int j = 0; j < kBatch; ++j) sb[j] = scale_at(cur.mu(j), j);
       }
     }
     for (int b = 0; b < nfull; ++b) {
@@ -457,7 +463,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
       for (int j = 0; j < kBatch; ++j) {
         if (OCT && j == kBatch / 2 && b + 1 < nfull) {
 #pragma unroll
-          for (int q = 0; q < kBatch; ++q) sbn[q] = srow[(octave_of(nxt.mu(q), er[q % PER]) << lgD) + cb[q % PER]].x;
+          for (int q = 0; q < kBatch; ++q) sbn[q] = scale_at(nxt.mu(q), q);
         }
         uint32_t c, f;
         model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), OCT ? sb[j] : s[j % PER], c, f);

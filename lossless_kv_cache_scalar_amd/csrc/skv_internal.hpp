@@ -123,6 +123,16 @@ __device__ __forceinline__ float bf16_lo_edge(uint32_t b) {
   return lo;
 }
 
+// a pointer that is the same for the whole wave, moved to scalar registers so
+// that loads through it take a scalar base and a 32-bit lane offset
+template <typename T>
+__device__ __forceinline__ const T *wave_uniform(const T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<const T *>(((uint64_t)hi << 32) | lo);
+}
+
 // octave of a scalar with finite mean m in a channel with reference eref
 __device__ __forceinline__ uint32_t octave_of(float m, int32_t eref) {
   const int32_t e = (int32_t)((__float_as_uint(m) >> 23) & 0xFFu);
