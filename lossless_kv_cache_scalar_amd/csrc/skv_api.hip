@@ -201,7 +201,7 @@ extern "C" int skv_encode(const skv_shape *shape, const void *x, const void *mu,
   if (workspace_bytes < layout(g).total) return SKV_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Workspace ws = carve(g, workspace);
-  if ((e = hip_status(launch_clear_status(status, st))) != SKV_OK) return e;
+  if ((e = hip_status(launch_clear_status(status, ws.ctr, st))) != SKV_OK) return e;
   if ((e = hip_status(launch_model(g, sigma, hist, ws, status, st))) != SKV_OK) return e;
   return hip_status(launch_encode(g, x, mu, ws, bits, bits_cap, offsets, status, st));
 }
@@ -218,7 +218,7 @@ extern "C" int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bi
   if (workspace_bytes < layout(g).total) return SKV_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Workspace ws = carve(g, workspace);
-  if ((e = hip_status(launch_clear_status(status, st))) != SKV_OK) return e;
+  if ((e = hip_status(launch_clear_status(status, ws.ctr, st))) != SKV_OK) return e;
   if ((e = hip_status(launch_model(g, sigma, hist, ws, status, st))) != SKV_OK) return e;
   return hip_status(launch_decode(g, bits, bits_bytes, offsets, mu, ws, x_out, status, st));
 }

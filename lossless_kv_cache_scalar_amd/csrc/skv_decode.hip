@@ -45,6 +45,7 @@ struct DecArgs {
   float inv_step;  // kNInv / MG
   void *x_out;
   int32_t *status;
+  uint32_t *ctr;   // next chunk id (zeroed by the call before the launch)
 };
 
 // Bits of one lane's substream, most significant first; bytes at or past its
@@ -408,11 +409,15 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
   constexpr bool BF = SYM == SKV_SYM_BF16;
   const Geo &g = a.g;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const uint32_t D = (uint32_t)g.D;
   constexpr int kStep = kLanes * kBatch;  // scalars of one batch of the wave
-  for (int64_t chunk = (int64_t)blockIdx.x * kDecWaves + wave; chunk < g.n_chunks;
-       chunk += (int64_t)gridDim.x * kDecWaves) {
+  for (;;) {
+    // chunk ids in increasing order from a counter: a wave that finishes
+    // early takes more, so no wave waits on a fixed share at the end
+    uint32_t cid = 0;
+    if (lane == 0) cid = atomicAdd(a.ctr, 1u);
+    const int64_t chunk = (int64_t)__builtin_amdgcn_readfirstlane(__shfl(cid, 0, 64));
+    if (chunk >= g.n_chunks) break;
     const int64_t row = chunk / g.ntb, blk = chunk - row * g.ntb;
     const int64_t tok = min<int64_t>(kChunkTokens, g.tokens - blk * kChunkTokens);
     const int nsc = (int)(tok * g.D);
@@ -625,7 +630,7 @@ static void launch_dec_kernel(const DecArgs &a, hipStream_t st) {
 hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes, const uint64_t *offsets,
                          const void *mu, const Workspace &ws, void *x_out, int32_t *status, hipStream_t st) {
   DecArgs a{g, bits, bits_bytes, offsets, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.uinv, ws.etab,
-            ws.scale, ws.eref, (float)kNInv / (float)g.MG, x_out, status};
+            ws.scale, ws.eref, (float)kNInv / (float)g.MG, x_out, status, ws.ctr};
   timing_mark(kTimeDecode, false, st);
   if (g.sym_fmt == SKV_SYM_BF16) {
     if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_BF16, SKV_MU_BF16>(a, st);

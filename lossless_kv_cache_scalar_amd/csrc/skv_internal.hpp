@@ -187,7 +187,7 @@ hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Work
                          uint64_t bits_cap, uint64_t *offsets, int32_t *status, hipStream_t st);
 hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes, const uint64_t *offsets, const void *mu,
                          const Workspace &ws, void *x_out, int32_t *status, hipStream_t st);
-hipError_t launch_clear_status(int32_t *status, hipStream_t st);
+hipError_t launch_clear_status(int32_t *status, uint32_t *ctr, hipStream_t st);
 hipError_t launch_calib_reset(const Geo &g, void *state, hipStream_t st);
 hipError_t launch_calib_accumulate(const Geo &g, void *state, const void *x, const void *mu, hipStream_t st);
 hipError_t launch_calib_finalize(const Geo &g, const void *state, float *sigma, uint64_t *hist, hipStream_t st);

@@ -245,12 +245,17 @@ __global__ void k_scale_oct(const float *__restrict__ table, float2 *__restrict_
   if (bad) set_status(status, SKV_ERR_ARG);
 }
 
-__global__ void k_clear_status(int32_t *status) {
-  if (threadIdx.x == 0) *status = SKV_OK;
+// the call's status, and the workspace's chunk counter (the kernels take
+// chunk ids from it)
+__global__ void k_clear_status(int32_t *status, uint32_t *ctr) {
+  if (threadIdx.x == 0) {
+    *status = SKV_OK;
+    *ctr = 0;
+  }
 }
 
-hipError_t launch_clear_status(int32_t *status, hipStream_t st) {
-  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, st, status);
+hipError_t launch_clear_status(int32_t *status, uint32_t *ctr, hipStream_t st) {
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, st, status, ctr);
   return hipGetLastError();
 }
 
