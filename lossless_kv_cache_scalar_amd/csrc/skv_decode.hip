@@ -2,8 +2,10 @@
 //
 // Persistent grid, one 1024-thread block per CU with the model's tables in
 // LDS (knots 16 KB, the inverse of the Gaussian pair's CDF 8 KB, the bf16 p_hat
-// table 137 KB).  Each wavefront decodes whole chunks; lane l decodes
-// substream l, the chunk's scalars l, l + 64, ...  The model is rebuilt from
+// table 137 KB).  Each wavefront decodes whole chunks, taking their ids from a
+// counter (the waves of a SIMD issue at different rates, so fixed shares would
+// leave the fast ones idle); lane l decodes substream l, the chunk's scalars
+// l, l + 64, ...  The model is rebuilt from
 // (mu, sigma, hist), as both ends of the coder do ("Speculative KV coding",
 // "什么能预测 KV 缓存").
 //
