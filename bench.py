@@ -50,9 +50,9 @@ def csrc_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources and on this workload."""
+def counter_record(kernel: str, workload: str):
+    """The committed rocprofv3 counter record of a kernel, if it was taken on the
+    current kernel sources and on this workload."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
@@ -60,7 +60,33 @@ def measured_traffic(kernel: str, workload: str):
         rec = json.load(fh)
     if rec.get("csrc_hash") != csrc_hash() or rec.get("workload") != workload:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter runs (FETCH_SIZE and
+    WRITE_SIZE scaled by a copy of known size), or None."""
+    rec = counter_record(kernel, workload)
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+# VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one pass of a 64-lane
+# instruction every 4 cycles (simple 32-bit adds, logic and fp32 fma can issue
+# faster, so a kernel made mostly of them can exceed it)
+VALU_PEAK_LANE_INSTR_PER_S = 256 * 4 * 16 * 2.4e9
+
+
+def valu_use(kernel: str, workload: str, n_symbols: int, launch_ms: float):
+    """VALU instructions per symbol from the committed SQ_INSTS_VALU counter run,
+    and the lane-instruction rate they imply at the measured launch time."""
+    rec = counter_record(kernel, workload)
+    if rec is None or not rec.get("valu_instr_per_symbol"):
+        return None
+    per = float(rec["valu_instr_per_symbol"])
+    rate = per * n_symbols / (launch_ms * 1e-3)
+    return {"instr_per_symbol": per, "achieved": round(rate / 1e12, 3), "peak": round(VALU_PEAK_LANE_INSTR_PER_S / 1e12, 3),
+            "unit": "T lane-instr/s", "frac": round(rate / VALU_PEAK_LANE_INSTR_PER_S, 4),
+            "source": "SQ_INSTS_VALU x 64 / symbols, counter run on the same kernel sources"}
 
 
 def main():
@@ -208,6 +234,9 @@ def main():
             "bytes_per_launch": moved,
             "bytes_per_scalar": round(moved / n, 5),
             "launch_ms": round(kms, 4),
+            # the codec's kernels are bound by VALU issue, not by HBM: the
+            # fraction of the VALU issue rate the dominant kernel reaches
+            "valu": valu_use(kern, w.name, n, kms),
         },
         "kernel_ms": {k: round(v, 4) for k, v in sorted(kern_avg.items())},
         "cpu_baseline": None,
