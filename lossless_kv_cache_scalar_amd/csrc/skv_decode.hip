@@ -573,14 +573,28 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
   }
 }
 
+// The decoder's LDS tables in one block, the small ones first: every table
+// then starts below 64 KB, so a table read takes its base as the LDS
+// instruction's immediate offset and its index by one shift (a separate base
+// register costs a three-operand shift-add, twice the issue time of a shift).
+template <bool BF>
+struct DecLds {
+  float2 kn[kNKnot];
+  float2 ui[kNInv + 1];
+  uint32_t ab[BF ? kNWin + 2 : 512];  // (even length: the next table stays 8-byte aligned)
+  float2 et[BF ? 1 : 256];
+  uint32_t a16w[BF ? kNWin * kWinEntries / 2 : 1];
+};
+
 template <int SYM, int MU, int PER, int OCT>
 __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
-  __shared__ float2 s_kn[kNKnot];
-  __shared__ float2 s_ui[kNInv + 1];
-  __shared__ uint32_t s_a16w[BF ? kNWin * kWinEntries / 2 : 1];
-  __shared__ __align__(8) uint32_t s_ab[BF ? kNWin + 1 : 512];
-  __shared__ float2 s_et[BF ? 1 : 256];
+  __shared__ DecLds<BF> lds;
+  float2 *s_kn = lds.kn;
+  float2 *s_ui = lds.ui;
+  uint32_t *s_a16w = lds.a16w;
+  uint32_t *s_ab = lds.ab;
+  float2 *s_et = lds.et;
 
   const bool win = BF ? *a.aflag != 0 : true;
   for (int i = threadIdx.x; i < kNKnot; i += kDecBlock) s_kn[i] = a.knots[i];

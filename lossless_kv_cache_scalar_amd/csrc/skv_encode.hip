@@ -535,13 +535,26 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
   }
 }
 
+// The encoder's LDS tables in one block, the small ones first: every table
+// then starts below 64 KB, so a table read takes its base as the LDS
+// instruction's immediate offset and its index by one shift (a separate base
+// register costs a three-operand shift-add, twice the issue time of a shift).
+template <bool BF>
+struct EncLds {
+  float2 kn[kNKnot];
+  uint32_t ab[BF ? kNWin + 2 : 512];  // (even length: the next table stays 8-byte aligned)
+  float2 et[BF ? 1 : 256];
+  uint32_t a16w[BF ? kNWin * kWinEntries / 2 : 1];
+};
+
 template <int SYM, int MU, int PER, int OCT>
 __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
-  __shared__ float2 s_kn[kNKnot];
-  __shared__ uint32_t s_a16w[BF ? kNWin * kWinEntries / 2 : 1];
-  __shared__ __align__(8) uint32_t s_ab[BF ? kNWin + 1 : 512];
-  __shared__ float2 s_et[BF ? 1 : 256];
+  __shared__ EncLds<BF> lds;
+  float2 *s_kn = lds.kn;
+  uint32_t *s_a16w = lds.a16w;
+  uint32_t *s_ab = lds.ab;
+  float2 *s_et = lds.et;
 
   const bool fast = BF ? *a.aflag != 0 : true;  // windowed p_hat table usable
   for (int i = threadIdx.x; i < kNKnot; i += kEncBlock) s_kn[i] = a.knots[i];
