@@ -63,6 +63,7 @@ struct LaneReader {
   uint32_t m;            // interleaved words per lane
   uint32_t tail, len;    // chunk offset of the lane's tail, lane length
   uint32_t ip0;          // chunk offset of the lane's interleaved word 0 (word w: ip0 + 256 w)
+  uint32_t ipw;          // ip0 + 256 w, advanced with w (an add where the product would take a shift-add)
   uint32_t w, plo, phi;
   uint64_t ib;  // next bits, left-aligned
   int nib;      // valid bits in ib
@@ -72,7 +73,7 @@ struct LaneReader {
   __device__ __forceinline__ void issue() {
     const bool tl = w >= m;
     fast = !__any(tl);
-    uint32_t a0 = ip0 + (w << 8);  // an interleaved word never lies past the lane's end
+    uint32_t a0 = ipw;  // = ip0 + 256 w; an interleaved word never lies past the lane's end
     if (__builtin_expect(!fast, 0)) {
       if (tl) {
         a0 = (tail + 4u * (w - m)) & ~3u;
@@ -103,13 +104,16 @@ struct LaneReader {
   __device__ __forceinline__ void init(uint32_t lane) {
     w = 0;
     ip0 = kHeaderBytes + 4u * lane;
+    ipw = ip0;
     issue();
     ib = (uint64_t)word() << 32;
     w = 1;
+    ipw += 256u;
     issue();
     ib |= word();
     nib = 64;
     w = 2;
+    ipw += 256u;
     issue();
   }
   // n in {0, 8, 16, 24}
@@ -118,6 +122,7 @@ struct LaneReader {
       ib |= (uint64_t)word() << (32 - nib);
       nib += 32;
       ++w;
+      ipw += 256u;
     }
     const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)(ib >> 32), (0u - n) & 31u, n);
     ib <<= n;
@@ -131,6 +136,7 @@ struct LaneReader {
       ib |= (uint64_t)word() << (32 - nib);
       nib += 32;
       ++w;
+      ipw += 256u;
     }
     const uint64_t lo = (((uint64_t)(uint32_t)x << 32) | (uint32_t)(ib >> 32)) << n;
     const uint64_t r = ((x << n) & 0xFFFFFFFF00000000ull) | (lo >> 32);

@@ -306,24 +306,22 @@ __device__ __forceinline__ void a_pair_bf16(const EncArgs &a, const EncTables &t
 }
 
 // (c, f) of symbol b on the coder's 2^24 total, for every b but the special
-// bf16 ones (+-0, +-inf, NaN), which report special = true and need
-// model_special.  The bin of a finite non-zero bf16 b is [(b-1):8000, b:8000]
+// bf16 ones (+-0, +-inf, NaN), which need model_special: spm is the wave's
+// mask of lanes that may hold one (bf16_hi_bits).  The bin of a finite non-zero bf16 b is [(b-1):8000, b:8000]
 // in fp32 bits for b > 0 and the same pair swapped for b < 0; Cg is monotone,
 // so the lower count is the min of the two.
 template <int SYM, bool FAST>
 __device__ __forceinline__ void model_common(const EncArgs &a, const EncTables &t, uint32_t b, float m, float sj,
-                                             uint32_t &c, uint32_t &f, bool &special) {
+                                             uint32_t &c, uint32_t &f, uint64_t &spm) {
   if (SYM == SKV_SYM_BF16) {
     // p_hat part first: it depends on b alone, so its table reads are in flight
     // while the Gaussian pair is evaluated
     uint32_t alo, ahi;
     a_pair_bf16<FAST>(a, t, b, alo, ahi);
-    uint32_t eA;  // (b << 16) | 0x8000 as one shift-or
-    asm("v_lshl_or_b32 %0, %1, 16, %2" : "=v"(eA) : "v"(b), "s"(0x8000u));
+    const uint32_t eA = bf16_hi_bits(b, spm);  // (b << 16) | 0x8000
     const uint32_t eB = eA - 0x10000u;
     const uint32_t cA = cg_eval(t.kn, u_of(__uint_as_float(eA), m, sj));
     const uint32_t cB = cg_eval(t.kn, u_of(__uint_as_float(eB), m, sj));
-    special = ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17);
     c = alo + min(cA, cB);
     f = ahi + max(cA, cB) - c;
   } else {
@@ -333,7 +331,7 @@ __device__ __forceinline__ void model_common(const EncArgs &a, const EncTables &
     const uint32_t hi = p.y + cg_eval(t.kn, u_of(e.y, m, sj));
     c = lo << 8;
     f = (hi - lo) << 8;
-    special = false;
+    spm = 0;
   }
 }
 
@@ -352,10 +350,10 @@ __device__ __forceinline__ void model_special(const EncArgs &a, const EncTables 
 template <int SYM, bool FAST>
 __device__ __forceinline__ void model_pair(const EncArgs &a, const EncTables &t, uint32_t b, float m, float sj,
                                            uint32_t &c, uint32_t &f) {
-  bool special;
-  model_common<SYM, FAST>(a, t, b, m, sj, c, f, special);
-  if (SYM == SKV_SYM_BF16 && __builtin_expect(__any(special), 0)) {
-    if (special) model_special<FAST>(a, t, b, m, sj, c, f);
+  uint64_t spm;
+  model_common<SYM, FAST>(a, t, b, m, sj, c, f, spm);
+  if (SYM == SKV_SYM_BF16 && __builtin_expect(spm != 0, 0)) {
+    if (bf16_special(b)) model_special<FAST>(a, t, b, m, sj, c, f);
   }
 }
 

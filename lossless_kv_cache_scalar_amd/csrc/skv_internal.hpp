@@ -117,6 +117,25 @@ __device__ __forceinline__ void bf16_bin(uint32_t b, float &lo, float &hi) {
   hi = __uint_as_float(sgn ? (a | sgn) : c);
 }
 
+// (b << 16) | 0x8000 for a bf16 pattern b < 2^16: the fp32 bits of the bin
+// edge half an ulp beyond b's magnitude (the upper edge for b > 0, the lower
+// one for b < 0; the other edge is these bits less 0x10000).  spm gets the
+// wave's mask of lanes whose b may be special (+-0, +-inf, NaN: bins that need
+// bf16_bin), from one class test of the pattern read as fp32 (signaling and
+// quiet NaN, -inf, -0, +0, +inf), so the common case costs a shift, an or and
+// the test, and the branch on the mask is scalar.  A lane the test flags by
+// mistake would only take the general edges, which hold for every pattern.
+__device__ __forceinline__ uint32_t bf16_hi_bits(uint32_t b, uint64_t &spm) {
+  const uint32_t bf = b << 16;
+  // written out: the compiler's own form of this test goes through fp64
+  asm("v_cmp_class_f32_e64 %0, %1, %2" : "=s"(spm) : "v"(bf), "s"(0x267u));
+  uint32_t e;
+  asm("v_or_b32 %0, 0x8000, %1" : "=v"(e) : "v"(bf));  // an or, not the shift-or the compiler would fuse
+  return e;
+}
+// the lane's own test: magnitude 0 or at least 0x7F80
+__device__ __forceinline__ bool bf16_special(uint32_t b) { return ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17); }
+
 __device__ __forceinline__ float bf16_lo_edge(uint32_t b) {
   float lo, hi;
   bf16_bin(b, lo, hi);

@@ -68,16 +68,15 @@ __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float
     // count is the min of the two.  +-0, +-inf and NaN take the general edges
     // (the counts are complete before that rare branch, which redoes them, so
     // the table reads and their sums stay in one block).
-    uint32_t eA;  // (b << 16) | 0x8000 as one shift-or
-    asm("v_lshl_or_b32 %0, %1, 16, %2" : "=v"(eA) : "v"(b), "s"(0x8000u));
+    uint64_t spm;
+    const uint32_t eA = bf16_hi_bits(b, spm);  // (b << 16) | 0x8000
     const uint32_t eB = eA - 0x10000u;
     const uint32_t cA = cg_eval(t.kn, u_of(__uint_as_float(eA), m, s));
     const uint32_t cB = cg_eval(t.kn, u_of(__uint_as_float(eB), m, s));
     clo = alo + min(cA, cB);
     chi = ahi + max(cA, cB);
-    const bool special = ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17);
-    if (__builtin_expect(__any(special), 0)) {
-      if (special) {
+    if (__builtin_expect(spm != 0, 0)) {
+      if (bf16_special(b)) {
         a_pair<TAB>(t, tix_bf16(b), alo, ahi);
         float lo, hi;
         bf16_bin(b, lo, hi);
@@ -102,7 +101,7 @@ __device__ __forceinline__ uint32_t cum_rank(const ModelTabs &t, uint32_t k, flo
     // (b < 0) in fp32 bits; +-0, +-inf and NaN take the general edge
     const uint32_t b = unrank_bf16(k);
     uint32_t e = (b & 0x8000u) ? ((b << 16) | 0x8000u) : ((b << 16) - 0x8000u);
-    const bool special = ((b << 17) - (1u << 17)) >= (0x7F7Fu << 17);
+    const bool special = bf16_special(b);
     if (__builtin_expect(__any(special), 0)) {
       if (special) e = __float_as_uint(bf16_lo_edge(b));
     }
