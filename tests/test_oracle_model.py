@@ -106,6 +106,41 @@ def test_cg_monotone_and_saturating(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_cg_monotone_over_every_fp32(fmt):
+    """Cg is non-decreasing over every fp32 knot coordinate in [-1024, 1024]
+    (about 2.2e9 values, walked in value order: the negative patterns from
+    -1024 down to -0 by decreasing bits, then +0 up to +1024), not only on
+    samples.  A non-decreasing Cg makes cum(k) non-decreasing in k for every
+    (mu, sigma), so the only source of each frequency's lower bound is the
+    one-count floor the model adds."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    m = R.Model(fmt)
+    top = int(np.float32(1024.0).view(np.uint32)) + 1   # patterns 0 .. 0x44800000
+    chunk = 1 << 24
+    # pieces in value order: (lo, hi, negative) over magnitude bit patterns
+    pieces = [(max(0, h - chunk), h, True) for h in range(top, 0, -chunk)]
+    pieces += [(lo, min(top, lo + chunk), False) for lo in range(0, top, chunk)]
+
+    def run(piece):
+        lo, hi, neg = piece
+        if neg:  # decreasing magnitude: increasing value
+            bits = np.arange(hi - 1, lo - 1, -1, dtype=np.uint32) | np.uint32(0x80000000)
+        else:
+            bits = np.arange(lo, hi, dtype=np.uint32)
+        cg = m.cg(bits.view(np.float32)).astype(np.int64)
+        return int(cg[0]), int(cg[-1]), bool(np.all(np.diff(cg) >= 0))
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        res = list(ex.map(run, pieces))
+    prev = -1
+    for (lo, hi, neg), (first, last, inside) in zip(pieces, res):
+        assert inside and first >= prev, f"Cg decreases in the {'negative' if neg else 'positive'} patterns {lo:#x}..{hi:#x}"
+        prev = last
+    assert res[0][0] == 0 and prev == m.MG
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_cg_within_interpolation_bound_of_exact(fmt):
     """Linear interpolation between knots h = 1/64 apart is within h^2/8 max|G''|
     of the exact mixture CDF; knot rounding adds 1/2 count and the floor 1."""
