@@ -92,8 +92,8 @@ def valu_use(kernel: str, workload: str, n_symbols: int, launch_ms: float):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on one GPU only: the coding path is per-chunk independent and this build "
-              f"measures one GPU's share (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: chunks code independently, and it measures one GPU's share "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -48,7 +48,7 @@ def load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise SkvError(f"libskv is not built ({LIB_PATH} missing); run __graft_entry__.build()")
+        raise SkvError(f"libskv is not built ({LIB_PATH} missing); run python -m lossless_kv_cache_scalar_amd.build")
     L = C.CDLL(LIB_PATH)
     vp, i64, sz, i32p = C.c_void_p, C.c_int64, C.c_size_t, C.c_void_p
     sp = C.POINTER(SkvShape)
