@@ -252,6 +252,45 @@ def test_e4m3_bins_are_saturating_rne_preimages():
     assert lo[0x7E] == 432.0 and hi[0x7E] == np.inf and lo[0x01] == 2.0 ** -10
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_every_fp32_rounds_into_its_symbols_bin(fmt):
+    """Every fp32 value that is not a NaN (about 4.28e9) rounds, by torch's
+    conversion (nearest even; e4m3 saturating at +-448), to a symbol whose
+    oracle bin [lo, hi] contains it: the bins cover the whole real line with
+    each value in the bin of the symbol it rounds to, not only at the edges."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n_sym = 65536 if fmt == 0 else 256
+    LO, HI = R.bins(fmt, np.arange(n_sym, dtype=np.uint32))
+    chunk = 1 << 24
+
+    def sym(y):
+        t = torch.from_numpy(y)
+        if fmt == 0:
+            return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return t.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    def run(start):
+        bits = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        nan = ((bits & 0x7F800000) == 0x7F800000) & ((bits & 0x007FFFFF) != 0)
+        y = bits[~nan].view(np.float32)
+        s_ = sym(y)
+        ok = (LO[s_] <= y) & (y <= HI[s_])
+        if ok.all():
+            return None
+        i = int(np.flatnonzero(~ok)[0])
+        return float(y[i]), int(s_[i]), float(LO[s_[i]]), float(HI[s_[i]])
+
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)  # the chunks run in parallel threads instead
+    try:
+        with ThreadPoolExecutor(max_workers=6) as ex:
+            bad = [r for r in ex.map(run, range(0, 1 << 32, chunk)) if r is not None]
+    finally:
+        torch.set_num_threads(threads)
+    assert not bad, f"value outside its symbol's bin (y, symbol, lo, hi): {bad[:3]}"
+
+
 def test_bf16_bin_ends_meet_in_rank_order():
     b = np.array([R.unrank(0, k) for k in range(65536)], dtype=np.uint32)
     lo, hi = R.bins(0, b)
