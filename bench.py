@@ -274,17 +274,23 @@ def cpu_baseline(w, x, mu, sigma, hist, buf, seconds):
                if n_rows % 2 == 0 else None)
         return xs, ms, shp
 
-    def run(n_rows):
+    def run(n_rows, threads=cores):
         xs, ms, shp = sample(n_rows)
         sig = np.ascontiguousarray(rsig[: n_rows * w.head_dim * per_ch])
         t0 = time.perf_counter()
-        bits, offs = model.encode(shp, xs, ms, sig, nthreads=cores)
+        bits, offs = model.encode(shp, xs, ms, sig, nthreads=threads)
         t1 = time.perf_counter()
-        dec, st = model.decode(shp, bits, offs, ms, sig, nthreads=cores)
+        dec, st = model.decode(shp, bits, offs, ms, sig, nthreads=threads)
         t2 = time.perf_counter()
         return xs, bits, offs, dec, st, t1 - t0, t2 - t1
 
-    # size the sample: one row first, then as many rows as fit the time budget
+    # one core on one (layer, kv) pair of rows
+    xs1, _, _, dec1, st1, te1, td1 = run(2, threads=1)
+    raw1 = xs1.size * w.sym_bytes
+    single = {"encode_GBps": round(raw1 / te1 / 1e9, 5), "decode_GBps": round(raw1 / td1 / 1e9, 5),
+              "value": round(raw1 / (te1 + td1) / 1e9, 5), "sample": f"2 rows, {xs1.size} scalars, 1 thread",
+              "roundtrip_exact": bool(st1 == R.OK and np.array_equal(dec1, xs1))}
+    # size the sample: one row pair first, then as many rows as fit the time budget
     _, _, _, _, _, te, td = run(2)
     per_row = (te + td) / 2
     n_rows = int(max(2, min(w.layers * rows_per_layer, seconds / max(per_row, 1e-6))))
@@ -307,6 +313,7 @@ def cpu_baseline(w, x, mu, sigma, hist, buf, seconds):
         "encode_GBps": round(raw / te / 1e9, 5),
         "decode_GBps": round(raw / td / 1e9, 5),
         "seconds": round(te + td, 3),
+        "single_core": single,
         "gpu_bytes_match_oracle": same,
         "oracle_roundtrip_exact": bool(st == R.OK and np.array_equal(dec, xs)),
     }
