@@ -303,10 +303,17 @@ def cpu_baseline(w, x, mu, sigma, hist, buf, seconds):
     goffs = buf.offsets[: nchunks + 1].cpu().numpy().view(np.uint64)
     gbits = buf.bits[: int(goffs[-1])].cpu().numpy()
     same = bool(np.array_equal(goffs, offs) and np.array_equal(gbits, bits))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(raw / (te + td) / 1e9, 5),
         "unit": "GB/s",
         "cores": cores,
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"{n_rows} of {w.layers * rows_per_layer} (layer, kv, head) rows = {nchunks} chunks, "
                   f"{n} scalars, encode + decode",
