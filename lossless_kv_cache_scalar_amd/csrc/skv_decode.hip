@@ -378,7 +378,11 @@ __device__ __forceinline__ void resolve_misses(const ModelTabs &t, bool miss, bo
 }
 
 // Decode one symbol of a lane: returns its pattern and advances the coder.
-template <int SYM, int MU, int TAB>
+// FULL: every lane of the wave is active (full batches), so a miss is always
+// resolved by the whole wave and the lane-alone search is not compiled in; the
+// batch loop inlines this eight times, and the smaller code stays in the
+// instruction cache.
+template <int SYM, int MU, int TAB, bool FULL>
 __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelTabs &t, const float2 *uinv,
                                                   LaneReader &br, uint64_t &d, uint64_t &range,
                                                   bool &corrupt, float m, uint32_t mraw, float sj, float sinvj) {
@@ -402,7 +406,7 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   bool below;
   const bool ok = verify<SYM, TAB>(t, gs, m, sj, d, r, up, clo, chi, dd, pf, below);
   if (__builtin_expect(__any(!ok), 0)) {
-    if (__ballot(1) == ~0ull) resolve_misses<SYM, TAB>(t, !ok, below, gs, clo, chi, m, sj, d, r, dd, pf, corrupt);
+    if (FULL || __ballot(1) == ~0ull) resolve_misses<SYM, TAB>(t, !ok, below, gs, clo, chi, m, sj, d, r, dd, pf, corrupt);
     else resolve_alone<SYM, TAB>(t, ok, below, gs, clo, chi, m, sj, d, r, dd, pf, corrupt);
   }
   // ---- update and renormalise
@@ -529,7 +533,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const uint32_t gs =
-            decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, OCT ? mj[j] : cur.get(j), cur.v[j],
+            decode_symbol<SYM, MU, TAB, true>(a, t, uinv, br, d, range, corrupt, OCT ? mj[j] : cur.get(j), cur.v[j],
                                         OCT ? sb[j].x : s[j % PER], OCT ? sb[j].y : sinv[j % PER]);
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
@@ -568,7 +572,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
           }
         }
       }
-      const uint32_t gs = decode_symbol<SYM, MU, TAB>(a, t, uinv, br, d, range, corrupt, m, mraw, sj, sij);
+      const uint32_t gs = decode_symbol<SYM, MU, TAB, false>(a, t, uinv, br, d, range, corrupt, m, mraw, sj, sij);
       br.issue();
       if (BF) static_cast<uint16_t *>(x_ch)[i] = (uint16_t)gs;
       else static_cast<uint8_t *>(x_ch)[i] = (uint8_t)gs;
