@@ -146,19 +146,24 @@ def main():
                           "csrc_hash": csrc_hash()}), flush=True)
         return
 
+    # encode and decode report into separate status words, so both are known
+    # after the timed steps without a synchronisation between the two calls
+    dstatus = torch.zeros(1, dtype=torch.int32, device=dev)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         buf.encode(x, mu, sigma, hist, stream)
         if ev is not None:
             ev[1].record(stream)
-        buf.decode(mu, sigma, hist, out, stream=stream)
+        buf.decode(mu, sigma, hist, out, stream=stream, status=dstatus)
         if ev is not None:
             ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    copy_gbps = measured_copy_peak(torch, dev)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     # per-kernel HIP events, recorded by the library on the launch stream
     skv.timing_start(8 * args.steps + 8)
@@ -177,7 +182,9 @@ def main():
     dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in events]))
     ms_per_step = wall * 1000.0 / args.steps
 
-    status = int(buf.status.item())
+    enc_status = int(buf.status.item())
+    dec_status = int(dstatus.item())
+    status = enc_status if enc_status != skv.OK else dec_status
     exact = bool(torch.equal(out, x))
     nbytes = buf.stream_bytes()
     n = w.n_scalars
@@ -193,6 +200,21 @@ def main():
     kern = "k_decode" if kern_avg["k_decode"] >= kern_avg["k_encode"] else "k_encode"
     kms = kern_avg[kern]
     traffic = measured_traffic(kern, w.name)
+    hbm_gbps = moved / kms / 1e6
+    hbm = {"achieved": round(hbm_gbps, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": round(hbm_gbps / HBM_PEAK_GBPS, 5), "traffic": traffic, "bytes_per_launch": moved,
+           "bytes_per_scalar": round(moved / n, 5), "measured_copy_peak": round(copy_gbps, 1),
+           "frac_of_measured_copy_peak": round(hbm_gbps / copy_gbps, 5)}
+    valu = valu_use(kern, w.name, n, kms)
+    if valu is not None and valu["frac"] > hbm["frac"]:
+        # the counters say the kernel is limited by VALU issue: that is its roofline
+        roofline = {"kernel": kern, "bound": "alu", "achieved": valu["achieved"], "peak": valu["peak"],
+                    "unit": valu["unit"], "frac": valu["frac"], "traffic": traffic, "launch_ms": round(kms, 4),
+                    "work": f"{valu['instr_per_symbol']} VALU instructions per symbol (SQ_INSTS_VALU x 64 / symbols "
+                            "on the same kernel sources; the method fixes no operation count)",
+                    "hbm": hbm}
+    else:
+        roofline = {"kernel": kern, "bound": "hbm", "launch_ms": round(kms, 4), **hbm, "valu": valu}
 
     result = {
         "metric": METRIC,
@@ -223,30 +245,38 @@ def main():
         "stream_bytes": nbytes,
         "roundtrip_exact": exact,
         "status": skv.status_string(status),
-        "roofline": {
-            "kernel": kern,
-            "bound": "hbm",
-            "achieved": round(moved / kms / 1e6, 3),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(moved / kms / 1e6 / HBM_PEAK_GBPS, 5),
-            "traffic": traffic,
-            "bytes_per_launch": moved,
-            "bytes_per_scalar": round(moved / n, 5),
-            "launch_ms": round(kms, 4),
-            # the codec's kernels are bound by VALU issue, not by HBM: the
-            # fraction of the VALU issue rate the dominant kernel reaches
-            "valu": valu_use(kern, w.name, n, kms),
-        },
+        "roofline": roofline,
         "kernel_ms": {k: round(v, 4) for k, v in sorted(kern_avg.items())},
         "cpu_baseline": None,
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, mu, sigma, hist, buf, args.cpu_seconds)
+    result["encode_status"] = skv.status_string(enc_status)
+    result["decode_status"] = skv.status_string(dec_status)
     print(json.dumps(result), flush=True)
     if not exact or status != skv.OK:
         sys.exit(1)
+
+
+def measured_copy_peak(torch, dev, reps=10):
+    """HBM bandwidth of a plain device copy of 1 GiB (1 GiB read + 1 GiB
+    written per copy), the median of `reps` timed copies, in GB/s."""
+    src = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    times.sort()
+    return 2.0 * (1 << 30) / (times[len(times) // 2] * 1e-3) / 1e9
 
 
 def cpu_baseline(w, x, mu, sigma, hist, buf, seconds):

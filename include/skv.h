@@ -61,7 +61,9 @@ enum skv_status {
   SKV_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
   SKV_ERR_CAPACITY = 4,     /* the compressed stream does not fit bits_cap */
   SKV_ERR_CORRUPT = 5,      /* the stream does not decode consistently */
-  SKV_ERR_TABLE = 6         /* histogram total too large for the p_hat table (Mp * total >= 2^64) */
+  SKV_ERR_TABLE = 6         /* histogram too large for the p_hat table: its smoothed total
+                               H(N) = sum over patterns of (hist + 1), an exact integer, has
+                               Mp * H(N) > 2^62 (this includes a total beyond 2^64) */
 };
 
 enum skv_sym_fmt { SKV_SYM_BF16 = 0, SKV_SYM_E4M3 = 1 };
@@ -170,7 +172,7 @@ int skv_calibrate(const skv_shape *seq_shape, int64_t n_seq, const void *x, cons
  *           and >= 0 (sigma below 2^-100 is treated as 2^-100)
  *   hist    (device) u64 symbol histogram as produced by skv_calib_finalize
  *   bits    (device) output stream, bits_cap bytes (>= skv_encode_bound
- *           guarantees success); 16-byte aligned
+ *           guarantees success); 16-byte aligned, else SKV_ERR_ARG
  *   offsets (device) u64 [n_chunks + 1]: chunk c is bits[offsets[c], offsets[c+1]);
  *           offsets[n_chunks] is the stream's total size
  *   workspace (device) skv_workspace_size(shape) bytes

@@ -197,7 +197,8 @@ extern "C" int skv_encode(const skv_shape *shape, const void *x, const void *mu,
   int e = make_geo(shape, g);
   if (e != SKV_OK) return e;
   if (!x || !mu || !sigma || !hist || !bits || !offsets || !workspace || !status) return SKV_ERR_ARG;
-  if (!aligned16(x) || !aligned16(mu) || !aligned16(workspace)) return SKV_ERR_ARG;
+  // the chunk writes store u16 / u32 words at bits + offset, offsets being multiples of 4
+  if (!aligned16(x) || !aligned16(mu) || !aligned16(workspace) || !aligned16(bits)) return SKV_ERR_ARG;
   if (workspace_bytes < layout(g).total) return SKV_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Workspace ws = carve(g, workspace);

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(1024) void k_knots(float2 *__restrict__ out, uint32
 // H(k+1) = H(k) + hist[unrank(k)] + 1, Qhat(k) = floor(Mp H(k) / H(N));
 // A(k) = k + Qhat(k) carries the one-count floor of every symbol.  The
 // quotient is exact: an fp64 estimate, then integer correction steps.
-// Domain: Mp * H(N) < 2^62, else SKV_ERR_TABLE.
+// Domain: Mp * H(N) <= 2^62 with H(N) the exact sum, else SKV_ERR_TABLE and a
+// uniform table (every frequency still >= 1).
 __device__ __forceinline__ uint64_t floor_div(uint64_t num, uint64_t den) {
   uint64_t q = (uint64_t)((double)num / (double)den);  // within 2 of the quotient
 #pragma unroll
@@ -65,16 +66,25 @@ __device__ __forceinline__ uint64_t floor_div(uint64_t num, uint64_t den) {
 // offsets do not fit 16 bits.
 constexpr int kPtBlock = 1024;
 
+// Sums of counts saturate at 2^64 - 1: a total that reaches it is beyond the
+// table's domain anyway, and saturating addition of unsigned values is
+// min(exact sum, 2^64 - 1) whatever the order, so no wrapped total can pass
+// for a small one.
+__device__ __forceinline__ uint64_t sat_add(uint64_t a, uint64_t b) {
+  const uint64_t s = a + b;
+  return s < a ? ~0ull : s;
+}
+
 __device__ __forceinline__ uint64_t rank_count(const uint64_t *__restrict__ hist, uint32_t k, int bf16) {
-  return hist[bf16 ? unrank_bf16(k) : unrank_e4m3(k)] + 1;
+  return sat_add(hist[bf16 ? unrank_bf16(k) : unrank_e4m3(k)], 1);
 }
 
 __device__ __forceinline__ uint64_t block_sum(uint64_t v, uint64_t *red) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  for (int off = 32; off > 0; off >>= 1) v = sat_add(v, __shfl_xor(v, off, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   uint64_t s = 0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s = sat_add(s, red[i]);
   return s;
 }
 
@@ -99,8 +109,8 @@ __global__ __launch_bounds__(kPtBlock) void k_ptable(const uint64_t *__restrict_
   uint64_t base = 0, total = 0;
   for (uint32_t i = 0; i < nblk; ++i) {
     const uint64_t v = psum[i];
-    if (i < blockIdx.x) base += v;
-    total += v;
+    if (i < blockIdx.x) base = sat_add(base, v);
+    total = sat_add(total, v);
   }
   const uint32_t k = blockIdx.x * kPtBlock + t;
   const bool active = k < N;

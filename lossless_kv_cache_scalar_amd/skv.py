@@ -176,15 +176,17 @@ class Buffers:
         self.offsets = torch.empty(self.n_chunks + 1, dtype=torch.int64, device=device)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
 
-    def encode(self, x, mu, sigma, hist, stream=None) -> None:
+    def encode(self, x, mu, sigma, hist, stream=None, status=None) -> None:
+        """skv_encode into this object's stream; the status word is self.status unless given."""
         _check(encode(self.shape, x, mu, sigma, hist, self.bits, self.bits.numel(), self.offsets, self.workspace,
-                      self.ws_bytes, self.status, stream), "skv_encode")
+                      self.ws_bytes, self.status if status is None else status, stream), "skv_encode")
 
-    def decode(self, mu, sigma, hist, x_out, bits=None, offsets=None, stream=None) -> None:
+    def decode(self, mu, sigma, hist, x_out, bits=None, offsets=None, stream=None, status=None) -> None:
+        """skv_decode of this object's stream (or the given one); the status word is self.status unless given."""
         bits = self.bits if bits is None else bits
         offsets = self.offsets if offsets is None else offsets
         _check(decode(self.shape, bits, bits.numel(), offsets, mu, sigma, hist, x_out, self.workspace,
-                      self.ws_bytes, self.status, stream), "skv_decode")
+                      self.ws_bytes, self.status if status is None else status, stream), "skv_decode")
 
     def stream_bytes(self) -> int:
         return int(self.offsets[-1].item())

@@ -256,7 +256,7 @@ uint32_t skvref_cg(const ref_model *m, float u) {
 /* The empirical component p_hat: "the empirical bf16 symbol distribution   */
 /* measured on training data" ([SKV] "早期结果"), +1 smoothed.  Its integer */
 /* CDF in rank order: H(0) = 0, H(k+1) = H(k) + hist[unrank(k)] + 1,        */
-/* Qhat(k) = floor(Mp * H(k) / H(N)) (exact integers; domain Mp*H(N) < 2^62). */
+/* Qhat(k) = floor(Mp * H(k) / H(N)) (exact integers; domain Mp*H(N) <= 2^62). */
 /* The table stored is A(k) = k + Qhat(k): the "+k" term is the floor of    */
 /* one count per symbol that keeps every frequency >= 1.                    */
 /* ------------------------------------------------------------------------ */
@@ -264,7 +264,9 @@ static int build_ptable(ref_model *m, const uint64_t *hist) {
   uint64_t Htot = 0;
   for (uint32_t k = 0; k < m->N; k++) {
     uint64_t h = hist ? hist[skvref_unrank(m->fmt, k)] : 0;
-    if (Htot + h + 1 < Htot) return REF_ERR_TABLE;
+    /* H(N) is the exact integer sum: one that does not fit 64 bits is outside
+       the domain (Htot + h + 1 <= 2^64 - 1 iff h < 2^64 - 1 - Htot) */
+    if (h >= UINT64_MAX - Htot) return REF_ERR_TABLE;
     Htot += h + 1;
   }
   if (m->Mp != 0 && Htot > (1ull << 62) / m->Mp) return REF_ERR_TABLE;

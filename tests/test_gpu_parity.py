@@ -125,11 +125,12 @@ def test_every_e4m3_pattern(mu_fmt):
     np.testing.assert_array_equal(out.cpu().numpy(), x)
 
 
-@pytest.mark.parametrize("tokens,head_dim,sym", [(1, 64, 0), (3, 128, 0), (300, 64, 1), (257, 8, 0), (40, 512, 1),
-                                                 (511, 16, 0), (2, 32, 1)])
-def test_ragged_shapes(tokens, head_dim, sym):
-    w = synth.Workload("ragged", 1, 2, 3, head_dim, tokens, sym, 0, 0.02, 1, 64)
-    rng = np.random.default_rng(tokens + head_dim)
+@pytest.mark.parametrize("tokens,head_dim,sym,mu_fmt", [
+    (1, 64, 0, 0), (3, 128, 0, 0), (300, 64, 1, 0), (257, 8, 0, 0), (40, 512, 1, 0), (511, 16, 0, 0), (2, 32, 1, 0),
+    (1, 64, 0, 1), (3, 128, 0, 1), (257, 8, 0, 1), (511, 16, 0, 1), (2, 32, 1, 1), (300, 64, 1, 1)])
+def test_ragged_shapes(tokens, head_dim, sym, mu_fmt):
+    w = synth.Workload("ragged", 1, 2, 3, head_dim, tokens, sym, mu_fmt, 0.02, 1, 64)
+    rng = np.random.default_rng(tokens + head_dim + 1000 * mu_fmt)
     x, mu = synth.generate(w)
     sigma = (0.02 * np.exp(rng.standard_normal(w.n_channels))).astype(np.float32)
     hist = rng.integers(0, 9, 65536 if sym == 0 else 256).astype(np.uint64)
@@ -137,7 +138,7 @@ def test_ragged_shapes(tokens, head_dim, sym):
     bits, offs, out, st_e, st_d = gpu_roundtrip(sh, x.to(DEV), mu.to(DEV), torch.from_numpy(sigma).to(DEV),
                                                 torch.from_numpy(hist.view(np.int64)).to(DEV))
     assert st_e == skv.OK and st_d == skv.OK
-    rbits, roffs = R.Model(sym, hist).encode(rsh, np_sym(x, sym), np_mu(mu, 0), sigma)
+    rbits, roffs = R.Model(sym, hist).encode(rsh, np_sym(x, sym), np_mu(mu, mu_fmt), sigma)
     np.testing.assert_array_equal(offs, roffs)
     np.testing.assert_array_equal(bits, rbits)
     assert torch.equal(out.cpu(), x)

@@ -1,0 +1,201 @@
+"""GPU parity on kernel paths that the workload cases do not reach, against the
+CPU oracle on the same seeded inputs (bytes, offsets, decoded symbols and
+status words bit-exact):
+
+* the bf16 p_hat table read from global memory, taken when a 64-rank window of
+  the table spans more than 65,535 counts (about a fifth of the calibration
+  mass on 64 neighbouring values: a cache with many exact zeros), in channel
+  and octave mode, with bf16 and fp32 means;
+* bf16 symbols with fp32 means, calibration included;
+* channel mode at head_dim 256 and 512 (scale periods 4 and 8), both symbol
+  formats and both mean formats;
+* the TABLE status (a histogram whose smoothed total is outside the table's
+  domain, a count whose +1 would wrap in 64 bits);
+* the decoder's lane-alone search, which runs only where a short chunk leaves
+  lanes idle and a guess misses (symbols far in the tails of their means).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_kv_cache_scalar_amd import skv, synth
+from oracle import skvref as R
+
+from gpu_util import DEV, ensure_built, gpu_calibrate, gpu_roundtrip, np_mu, np_sym, oracle_calibrate, shapes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+def _dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint64:
+        a = a.view(np.int64)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _check(sh, rsh, xn, mn, sigma, hist):
+    """GPU round trip through the C ABI; bytes, offsets and decoded symbols
+    equal the oracle's, and the oracle decodes the GPU stream."""
+    bits, offs, out, st_e, st_d = gpu_roundtrip(sh, _dev(xn), _dev(mn), _dev(sigma), _dev(hist))
+    assert st_e == skv.OK and st_d == skv.OK, (skv.status_string(st_e), skv.status_string(st_d))
+    model = R.Model(rsh.sym_fmt, hist)
+    rbits, roffs = model.encode(rsh, xn, mn, sigma)
+    np.testing.assert_array_equal(offs, roffs)
+    np.testing.assert_array_equal(bits, rbits)
+    np.testing.assert_array_equal(np_sym(out, rsh.sym_fmt), xn)
+    rout, st = model.decode(rsh, bits, offs, mn, sigma)
+    assert st == R.OK and np.array_equal(rout, xn)
+    return bits, offs
+
+
+def _max_window_span(hist):
+    """Largest A(64 w + 64) - A(64 w) of the oracle's bf16 table: above 65,535
+    the library cannot hold the table as 16-bit window offsets."""
+    A = R.Model(0, hist).ptable().astype(np.int64)
+    return int((A[64::64] - A[:-1:64]).max())
+
+
+def _sigma_for(w, rng, mode):
+    if mode == R.SIGMA_OCTAVE:
+        t = np.exp(rng.uniform(-7, 0, (w.n_channels, R.OCT_STRIDE))).astype(np.float32)
+        t[::5, 0] = 0.0
+        t[::7, 4] = 0.0
+        return np.ascontiguousarray(t.reshape(-1))
+    s = (0.02 * np.exp(rng.standard_normal(w.n_channels))).astype(np.float32)
+    s[::11] = 0.0
+    return s
+
+
+@pytest.mark.parametrize("mode", [R.SIGMA_CHANNEL, R.SIGMA_OCTAVE])
+@pytest.mark.parametrize("mu_fmt", [0, 1])
+@pytest.mark.parametrize("head_dim", [128, 512])
+def test_global_ptable_path(mode, mu_fmt, head_dim):
+    """A histogram with a spike at +0 (10^9 counts against ~3 million
+    elsewhere) puts one window's span far above 65,535, so the encoder and
+    decoder read p_hat from the global table."""
+    w = synth.Workload("spike", 4, 1, 2, head_dim, 600, 0, mu_fmt, 0.015, 1, 64, "mixture", mode)
+    rng = np.random.default_rng(11 + mode + 2 * mu_fmt + head_dim)
+    x, mu = synth.generate(w)
+    hist = rng.integers(0, 50, 65536).astype(np.uint64)
+    hist[0x0000] = 10 ** 9
+    assert _max_window_span(hist) > 0xFFFF
+    sh, rsh = shapes(w)
+    _check(sh, rsh, np_sym(x, 0), np_mu(mu, mu_fmt), _sigma_for(w, rng, mode), hist)
+
+
+def _zero_heavy(w, seed, frac=0.35):
+    x, mu = synth.generate(w, seed=seed)
+    g = torch.Generator().manual_seed(seed)
+    zero = torch.rand(x.shape, generator=g) < frac
+    x = x.clone()
+    x[zero] = 0
+    return x, mu
+
+
+@pytest.mark.parametrize("mode", [R.SIGMA_CHANNEL, R.SIGMA_OCTAVE])
+def test_zero_heavy_cache_calibrated(mode):
+    """A cache with 35% exact zeros, calibrated on a sequence of the same kind
+    on both sides: p_hat's +0 window is then too wide for the 16-bit image, and
+    calibration, encode and decode all match the oracle."""
+    w = synth.Workload("zeros", 4, 2, 2, 128, 600, 0, 0, 0.015, 2, 512, "mixture", mode)
+    seqs = [_zero_heavy(w, w.calib_seed(j)) for j in range(w.calib_seqs)]
+    seqs = [(x[:, :, :, : w.calib_tokens].contiguous(), m[:, :, :, : w.calib_tokens].contiguous()) for x, m in seqs]
+    sigma, hist = gpu_calibrate(w, seqs)
+    rsigma, rhist = oracle_calibrate(w, seqs)
+    np.testing.assert_array_equal(sigma.cpu().numpy(), rsigma)
+    np.testing.assert_array_equal(hist.cpu().numpy().view(np.uint64), rhist)
+    assert _max_window_span(rhist) > 0xFFFF
+    x, mu = _zero_heavy(w, w.data_seed)
+    sh, rsh = shapes(w)
+    _check(sh, rsh, np_sym(x, 0), np_mu(mu, 0), rsigma, rhist)
+
+
+@pytest.mark.parametrize("mode", [R.SIGMA_CHANNEL, R.SIGMA_OCTAVE])
+@pytest.mark.parametrize("sym", [0, 1])
+def test_fp32_means_calibration_and_coding(mode, sym):
+    """fp32 predictor means (bf16 symbols: never used by a workload) through
+    calibration, encode and decode, at 2 layers x 600 tokens."""
+    base = synth.WORKLOADS["qwen3_32b_bf16" if sym == 0 else "qwen3_0.6b_e4m3"]
+    w = dataclasses.replace(base, mu_fmt=1, sigma_mode=mode).with_tokens(600, layers=2)
+    seqs = [synth.calibration_set(w, j) for j in range(2)]
+    sigma, hist = gpu_calibrate(w, seqs)
+    rsigma, rhist = oracle_calibrate(w, seqs)
+    np.testing.assert_array_equal(sigma.cpu().numpy(), rsigma)
+    np.testing.assert_array_equal(hist.cpu().numpy().view(np.uint64), rhist)
+    x, mu = synth.generate(w)
+    assert mu.dtype == torch.float32
+    sh, rsh = shapes(w)
+    _check(sh, rsh, np_sym(x, sym), np_mu(mu, 1), rsigma, rhist)
+
+
+@pytest.mark.parametrize("tokens,head_dim,sym,mu_fmt", [
+    (300, 256, 0, 0), (40, 512, 0, 0), (300, 256, 0, 1), (600, 512, 0, 1),
+    (300, 256, 1, 0), (257, 256, 1, 1), (40, 512, 1, 1), (3, 256, 0, 1)])
+def test_channel_mode_wide_heads(tokens, head_dim, sym, mu_fmt):
+    """Channel-mode kernels with scale period 4 (head_dim 256) and 8 (512)."""
+    w = synth.Workload("wide", 1, 2, 2, head_dim, tokens, sym, mu_fmt, 0.02, 1, 64)
+    rng = np.random.default_rng(tokens + head_dim + 10 * sym + 100 * mu_fmt)
+    x, mu = synth.generate(w)
+    hist = rng.integers(0, 9, 65536 if sym == 0 else 256).astype(np.uint64)
+    sh, rsh = shapes(w)
+    _check(sh, rsh, np_sym(x, sym), np_mu(mu, mu_fmt), _sigma_for(w, rng, R.SIGMA_CHANNEL), hist)
+
+
+@pytest.mark.parametrize("tokens,head_dim", [(3, 8), (257, 8), (1, 16), (5, 8)])
+@pytest.mark.parametrize("sym", [0, 1])
+def test_lane_alone_search(tokens, head_dim, sym):
+    """Short chunks (fewer than 64 scalars, so lanes idle) whose symbols lie
+    far out in the tails of their means: the guesses miss and the decoder's
+    lane-alone secant, gallop and bisection find the symbols."""
+    rng = np.random.default_rng(tokens * 7 + head_dim + sym)
+    shape = (1, 2, 1, tokens, head_dim)
+    n = int(np.prod(shape))
+    far = np.ldexp(rng.uniform(1, 2, n), rng.integers(-12, 8, n)) * rng.choice([-1.0, 1.0], n)
+    near = rng.standard_normal(n)
+    val = np.where(rng.uniform(size=n) < 0.6, far, near).astype(np.float32).reshape(shape)
+    muf = (rng.standard_normal(n) * 0.01).astype(np.float32).reshape(shape)
+    if sym == 0:
+        xn = torch.from_numpy(val).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    else:
+        xn = torch.from_numpy(np.clip(val, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mn = torch.from_numpy(muf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    sigma = np.full(2 * head_dim, 0.003, dtype=np.float32)
+    # p_hat puts its mass on the far values, so their bins hold mostly p_hat counts
+    hist = np.zeros(65536 if sym == 0 else 256, dtype=np.uint64)
+    np.add.at(hist, xn.reshape(-1).astype(np.int64), 1000)
+    sh = skv.shape(1, 1, tokens, head_dim, sym, 0)
+    rsh = R.make_shape(1, 1, tokens, head_dim, sym, 0)
+    _check(sh, rsh, np.ascontiguousarray(xn), np.ascontiguousarray(mn), sigma, hist)
+
+
+@pytest.mark.parametrize("sym", [0, 1])
+@pytest.mark.parametrize("kind", ["over_limit", "wraps"])
+def test_table_status_matches_oracle(sym, kind):
+    """A histogram outside the p_hat table's domain: the oracle refuses the
+    model with TABLE, and the library reports TABLE from encode and decode
+    (it codes with the uniform table meanwhile, and stays consistent)."""
+    N = 65536 if sym == 0 else 256
+    Mp = R.Model(sym).Mp
+    rng = np.random.default_rng(5 + sym)
+    hist = rng.integers(0, 9, N).astype(np.uint64)
+    if kind == "over_limit":
+        hist[7] = np.uint64((1 << 62) // Mp)  # the smoothed total is then past the limit
+    else:
+        hist[9] = np.uint64(2 ** 64 - 1)  # hist + 1 wraps to 0 in 64 bits
+    with pytest.raises(ValueError, match="status 6"):
+        R.Model(sym, hist)
+    w = synth.Workload("table", 1, 1, 2, 64, 300, sym, 0, 0.02, 1, 64)
+    x, mu = synth.generate(w)
+    sh, _ = shapes(w)
+    sigma = np.full(w.n_channels, 0.02, dtype=np.float32)
+    bits, offs, out, st_e, st_d = gpu_roundtrip(sh, x.to(DEV), mu.to(DEV), _dev(sigma), _dev(hist))
+    assert st_e == skv.ERR_TABLE and st_d == skv.ERR_TABLE
+    assert torch.equal(out.cpu(), x)

@@ -322,6 +322,44 @@ def test_ptable_tracks_smoothed_histogram(fmt):
     assert A[0] == 0 and A[-1] == N + m.Mp
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_ptable_domain_edges(fmt):
+    """The p_hat table's domain is Mp * H(N) <= 2^62 for the exact smoothed
+    total H(N) = sum(hist + 1): at the largest admissible total the table is
+    the exact integer quotient (no 64-bit product overflows), one count more
+    is outside, and so is any histogram whose exact total passes 2^64 (a count
+    of 2^64 - 1 whose +1 would wrap to 0 in 64-bit arithmetic, or two large
+    counts)."""
+    N = 65536 if fmt == 0 else 256
+    Mp = R.Model(fmt).Mp
+    limit = (1 << 62) // Mp
+    hist = np.zeros(N, dtype=np.uint64)
+    pos = [R.unrank(fmt, k) for k in (3, N // 2, N - 2)]
+    hist[pos[0]] = limit // 3
+    hist[pos[1]] = limit // 5
+    hist[pos[2]] = limit - N - int(hist[pos[0]]) - int(hist[pos[1]])
+    assert int(hist.astype(object).sum()) + N == limit
+    A = R.Model(fmt, hist).ptable()
+    H = 0
+    want = []
+    for k in range(N):
+        want.append(k + Mp * H // limit)
+        H += int(hist[R.unrank(fmt, k)]) + 1
+    want.append(N + Mp)
+    assert A.tolist() == want
+    over = hist.copy()
+    over[pos[2]] += np.uint64(1)
+    for bad in (over, np.full(N, 0, dtype=np.uint64)):
+        if bad is not over:
+            bad[pos[1]] = np.uint64(2**64 - 1)
+        with pytest.raises(ValueError, match="status 6"):
+            R.Model(fmt, bad)
+    two = np.zeros(N, dtype=np.uint64)
+    two[pos[0]] = two[pos[1]] = np.uint64(2**63)
+    with pytest.raises(ValueError, match="status 6"):
+        R.Model(fmt, two)
+
+
 # ---------------------------------------------------------------- the integer model
 def _samples(fmt, n, seed):
     rng = np.random.default_rng(seed)
