@@ -61,9 +61,11 @@ enum skv_status {
   SKV_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
   SKV_ERR_CAPACITY = 4,     /* the compressed stream does not fit bits_cap */
   SKV_ERR_CORRUPT = 5,      /* the stream does not decode consistently */
-  SKV_ERR_TABLE = 6         /* histogram too large for the p_hat table: its smoothed total
+  SKV_ERR_TABLE = 6,        /* histogram too large for the p_hat table: its smoothed total
                                H(N) = sum over patterns of (hist + 1), an exact integer, has
                                Mp * H(N) > 2^62 (this includes a total beyond 2^64) */
+  SKV_ERR_SCRATCH = 7       /* skv_decode_static: the shape's decode workspace is larger than
+                               SKV_STATIC_SCRATCH_BYTES */
 };
 
 enum skv_sym_fmt { SKV_SYM_BF16 = 0, SKV_SYM_E4M3 = 1 };
@@ -202,6 +204,30 @@ int skv_encode(const skv_shape *shape, const void *x, const void *mu, const floa
 int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bits_bytes,
                const uint64_t *offsets, const void *mu, const float *sigma, const uint64_t *hist,
                void *x_out, void *workspace, size_t workspace_bytes, int32_t *status, void *stream);
+
+/*
+ * Decode without any allocation, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, outputs, status
+ * words and stream behaviour as skv_decode, less the workspace: the decode
+ * workspace (model tables, per-channel scales, chunk counter) lives in a
+ * static device array of SKV_STATIC_SCRATCH_BYTES inside the library, one
+ * copy per GPU, held until the process ends.  The first call on a device
+ * resolves that array's address (hipGetSymbolAddress) with the device
+ * current; no call allocates or frees memory, and the counter and status are
+ * cleared by a kernel (no memset).
+ * Limit: the shape's decode workspace must fit the array (16 MiB: about two
+ * million channels in channel mode, 230 thousand in octave mode, against
+ * 131,072 for the Qwen3-32B cache); a larger shape returns SKV_ERR_SCRATCH and
+ * enqueues nothing.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (two streams, two host threads) race
+ * and must be serialised by the caller.
+ */
+#define SKV_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int skv_decode_static(const skv_shape *shape, const uint8_t *bits, size_t bits_bytes,
+                      const uint64_t *offsets, const void *mu, const float *sigma, const uint64_t *hist,
+                      void *x_out, int32_t *status, void *stream);
 
 /* ---------------------------------------------------------------- kernel timing */
 

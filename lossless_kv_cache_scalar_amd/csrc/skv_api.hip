@@ -2,6 +2,8 @@
 // kernel launches on the caller's stream.  Declarations and contracts: skv.h.
 #include <math.h>
 
+#include <mutex>
+
 #include "skv_internal.hpp"
 
 using namespace skv;
@@ -15,6 +17,7 @@ extern "C" const char *skv_status_string(int status) {
     case SKV_ERR_CAPACITY: return "compressed stream exceeds the output capacity";
     case SKV_ERR_CORRUPT: return "corrupt stream";
     case SKV_ERR_TABLE: return "histogram too large for the p_hat table";
+    case SKV_ERR_SCRATCH: return "shape needs more than the library's static scratch (skv_decode_static)";
     default: return "unknown status";
   }
 }
@@ -62,7 +65,10 @@ struct Layout {
   size_t knots, ptab, a16, abase, aflag, psum, uinv, etab, scale, eref, flags, ctr, scratch, total;
 };
 
-Layout layout(const Geo &g) {
+// The workspace of a call: the model tables, the per-channel scales and the
+// chunk counter; an encode also needs the chunks' published sizes and its
+// scratch slots (enc = false leaves those two empty).
+Layout layout(const Geo &g, bool enc = true) {
   Layout L;
   size_t o = 0;
   L.knots = o; o = align_up(o + sizeof(float2) * kNKnot);
@@ -75,15 +81,15 @@ Layout layout(const Geo &g) {
   L.etab = o;  o = align_up(o + sizeof(float2) * 256);
   L.scale = o; o = align_up(o + sizeof(float2) * (size_t)(g.rows * g.D) * (g.octave ? kOctaves : 1));
   L.eref = o;  o = align_up(o + sizeof(int32_t) * (size_t)(g.octave ? g.rows * g.D : 1));
-  L.flags = o; o = align_up(o + sizeof(uint64_t) * (size_t)g.n_chunks);
+  L.flags = o; o = align_up(o + (enc ? sizeof(uint64_t) * (size_t)g.n_chunks : 0));
   L.ctr = o;   o = align_up(o + sizeof(uint32_t));
-  L.scratch = o; o = align_up(o + (size_t)g.n_chunks * kLanes * g.lane_cap);
+  L.scratch = o; o = align_up(o + (enc ? (size_t)g.n_chunks * kLanes * g.lane_cap : 0));
   L.total = o;
   return L;
 }
 
-Workspace carve(const Geo &g, void *base) {
-  Layout L = layout(g);
+Workspace carve(const Geo &g, void *base, bool enc = true) {
+  Layout L = layout(g, enc);
   uint8_t *b = static_cast<uint8_t *>(base);
   Workspace w;
   w.knots = reinterpret_cast<float2 *>(b + L.knots);
@@ -219,6 +225,58 @@ extern "C" int skv_decode(const skv_shape *shape, const uint8_t *bits, size_t bi
   if (workspace_bytes < layout(g).total) return SKV_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Workspace ws = carve(g, workspace);
+  if ((e = hip_status(launch_clear_status(status, ws.ctr, st))) != SKV_OK) return e;
+  if ((e = hip_status(launch_model(g, sigma, hist, ws, status, st))) != SKV_OK) return e;
+  return hip_status(launch_decode(g, bits, bits_bytes, offsets, mu, ws, x_out, status, st));
+}
+
+// ---------------------------------------------------------------- decode without allocation
+// skv_decode_static: the decode workspace (model tables, scales, chunk
+// counter) lives in this file-scope device array instead of a caller buffer.
+// Each GPU holds its own copy until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, resolved once per device (with that device current) on
+// the first call there, and only that address is passed to kernels.
+namespace {
+constexpr size_t kStaticScratchBytes = SKV_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void *g_static_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+int static_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SKV_ERR_HIP;
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return SKV_OK;
+}
+}  // namespace
+
+extern "C" int skv_decode_static(const skv_shape *shape, const uint8_t *bits, size_t bits_bytes,
+                                 const uint64_t *offsets, const void *mu, const float *sigma, const uint64_t *hist,
+                                 void *x_out, int32_t *status, void *stream) {
+  Geo g;
+  int e = make_geo(shape, g);
+  if (e != SKV_OK) return e;
+  if (!bits || !offsets || !mu || !sigma || !hist || !x_out || !status) return SKV_ERR_ARG;
+  if (!aligned16(mu) || !aligned16(x_out)) return SKV_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(bits) & 3u) || (bits_bytes & 3u)) return SKV_ERR_ARG;
+  if (layout(g, false).total > kStaticScratchBytes) return SKV_ERR_SCRATCH;
+  void *base = nullptr;
+  if ((e = static_scratch(&base)) != SKV_OK) return e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Workspace ws = carve(g, base, false);
+  // the counter and the status word are cleared by a kernel, not a memset
   if ((e = hip_status(launch_clear_status(status, ws.ctr, st))) != SKV_OK) return e;
   if ((e = hip_status(launch_model(g, sigma, hist, ws, status, st))) != SKV_OK) return e;
   return hip_status(launch_decode(g, bits, bits_bytes, offsets, mu, ws, x_out, status, st));

@@ -15,7 +15,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_lib", "libskv.so")
 
-OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLE = range(7)
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLE, ERR_SCRATCH = range(8)
+STATIC_SCRATCH_BYTES = 16 << 20  # SKV_STATIC_SCRATCH_BYTES
 SYM_BF16, SYM_E4M3 = 0, 1
 MU_BF16, MU_F32 = 0, 1
 SIGMA_CHANNEL, SIGMA_OCTAVE = 0, 1
@@ -25,7 +26,7 @@ OCT_STRIDE = 1 + OCTAVES
 # every function skv.h declares, in declaration order
 EXPORTS = ["skv_status_string", "skv_num_chunks", "skv_encode_bound", "skv_workspace_size",
            "skv_calib_state_size", "skv_calib_reset", "skv_calib_accumulate", "skv_calib_finalize",
-           "skv_calibrate", "skv_encode", "skv_decode", "skv_timing_start", "skv_timing_stop",
+           "skv_calibrate", "skv_encode", "skv_decode", "skv_decode_static", "skv_timing_start", "skv_timing_stop",
            "skv_timed_kernel_name"]
 
 
@@ -64,6 +65,7 @@ def load():
     L.skv_calibrate.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp]
     L.skv_encode.argtypes = [sp, vp, vp, vp, vp, vp, sz, vp, vp, sz, i32p, vp]
     L.skv_decode.argtypes = [sp, vp, sz, vp, vp, vp, vp, vp, vp, sz, i32p, vp]
+    L.skv_decode_static.argtypes = [sp, vp, sz, vp, vp, vp, vp, vp, i32p, vp]
     L.skv_timing_start.argtypes = [C.c_int32]
     L.skv_timing_stop.argtypes = [C.POINTER(C.c_int32), C.POINTER(C.c_float), C.c_int32, C.POINTER(C.c_int32)]
     L.skv_timed_kernel_name.argtypes = [C.c_int32]
@@ -160,6 +162,11 @@ def decode(sh: SkvShape, bits, bits_bytes: int, offsets, mu, sigma, hist, x_out,
            status, stream=None) -> int:
     return load().skv_decode(C.byref(sh), _ptr(bits), int(bits_bytes), _ptr(offsets), _ptr(mu), _ptr(sigma), _ptr(hist), _ptr(x_out),
                              _ptr(workspace), int(workspace_bytes), _ptr(status), _stream(stream))
+
+
+def decode_static(sh: SkvShape, bits, bits_bytes: int, offsets, mu, sigma, hist, x_out, status, stream=None) -> int:
+    return load().skv_decode_static(C.byref(sh), _ptr(bits), int(bits_bytes), _ptr(offsets), _ptr(mu), _ptr(sigma),
+                                    _ptr(hist), _ptr(x_out), _ptr(status), _stream(stream))
 
 
 # ---- buffers sized for a shape (torch allocates, the library fills) ----

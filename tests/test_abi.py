@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert skv.status_string(code)
     assert skv.status_string(99) == "unknown status"
 
@@ -95,3 +95,15 @@ def test_timing_argument_checks(lib):
     assert lib.skv_timing_stop(None, None, 4, C.byref(n)) == skv.ERR_ARG
     names = [skv.load().skv_timed_kernel_name(i).decode() for i in range(4)]
     assert names == ["model", "k_encode", "k_decode", "unknown"]
+
+
+def test_decode_static_host_checks(lib):
+    """skv_decode_static validates on the host before touching a device: null
+    pointers, and a shape whose decode workspace exceeds the static scratch."""
+    import ctypes as C
+    p = C.c_void_p(4096)  # never dereferenced: the calls below return before any launch
+    small = skv.shape(1, 1, 256, 64)
+    assert lib.skv_decode_static(C.byref(small), None, 0, p, p, p, p, p, p, None) == skv.ERR_ARG
+    huge = skv.shape(2048, 8, 256, 512, 0, 0, skv.SIGMA_OCTAVE)  # 16.8 million channels
+    assert lib.skv_decode_static(C.byref(huge), p, 4096, p, p, p, p, p, p, None) == skv.ERR_SCRATCH
+    assert skv.status_string(skv.ERR_SCRATCH).startswith("shape needs more")
