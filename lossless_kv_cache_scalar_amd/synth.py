@@ -19,6 +19,14 @@ cache geometry stands in for them:
   format (bf16, or kept fp32);
 * FP8 caches code e4m3(x) (round to nearest even, saturating at +-448).
 
+A drifting variant stands in for caches whose local statistics change along
+the sequence, the case the online-entropy-estimation page builds its adaptive
+counts for: each (layer, kv, head) row's scale is multiplied by
+exp(sin(2 pi t / 2048 + phi)), phi uniform per row, so the row's values and
+its residuals grow and shrink together over the tokens (about 2.7x either
+way), while sigma and p_hat are calibrated once, on sequences with their own
+phases.
+
 A second kind of predictor stands in for the FP8 model's own cache ("同一模型
 的优化版本": the predictor is a quantized copy of the same model): mu is the
 block-FP8 round trip of x itself, with one fp32 scale per 32 consecutive
@@ -52,8 +60,10 @@ class Workload:
     sigma_k: float        # sigma_c = sigma_k * s_c
     calib_seqs: int
     calib_tokens: int
-    mu_kind: str = "mixture"  # "mixture": x + sigma_c r; "fp8block": block-FP8 round trip of x
+    mu_kind: str = "mixture"  # "mixture": x + sigma_c r; "fp8block": block-FP8 round trip of x;
+                              # "drift": the mixture with a scale that drifts along tokens
     sigma_mode: int = 0       # how the coder resolves sigma: 0 per channel, 1 per channel and |mu| octave
+    phat_mode: int = 0        # p_hat: 0 the calibrated histogram, 1 adaptive (decayed counts per chunk)
 
     @property
     def model_seed(self) -> int:
@@ -85,7 +95,7 @@ class Workload:
     def with_tokens(self, tokens: int, layers: int | None = None, name: str | None = None) -> "Workload":
         return Workload(name or self.name, self.index, layers or self.layers, self.kv_heads, self.head_dim,
                         tokens, self.sym_fmt, self.mu_fmt, self.sigma_k, self.calib_seqs, self.calib_tokens,
-                        self.mu_kind, self.sigma_mode)
+                        self.mu_kind, self.sigma_mode, self.phat_mode)
 
 
 WORKLOADS = {
@@ -105,6 +115,12 @@ WORKLOADS = {
         Workload("qwen3_32b_bf16_fp8res", 6, 64, 8, 128, 8192, SYM_BF16, MU_BF16, 0.0, 128, 512, "fp8block"),
         # the same data coded with sigma per channel and octave of |mu| (same seeds)
         Workload("qwen3_32b_bf16_fp8res_oct", 6, 64, 8, 128, 8192, SYM_BF16, MU_BF16, 0.0, 128, 512, "fp8block", 1),
+        # Qwen3-0.6B FP8 cache geometry whose scale (values and residuals) drifts along tokens
+        Workload("qwen3_0.6b_e4m3_drift", 7, 28, 8, 128, 8192, SYM_E4M3, MU_F32, 0.05, 128, 512, "drift"),
+        # the same data coded with the adaptive p_hat (same seeds)
+        Workload("qwen3_0.6b_e4m3_drift_adapt", 7, 28, 8, 128, 8192, SYM_E4M3, MU_F32, 0.05, 128, 512, "drift", 0, 1),
+        # the 32K-token FP8 cache coded with the adaptive p_hat (same seeds as qwen3_32b_e4m3_32k)
+        Workload("qwen3_32b_e4m3_32k_adapt", 5, 64, 8, 128, 32768, SYM_E4M3, MU_BF16, 0.04, 128, 512, "mixture", 0, 1),
     ]
 }
 
@@ -152,11 +168,25 @@ def fp8_block_roundtrip(xf: torch.Tensor) -> torch.Tensor:
     return (q * scale).reshape(shp)
 
 
+DRIFT_PERIOD = 2048   # tokens
+DRIFT_AMPLITUDE = 1.0  # of the log scale
+
+
+def _drift(g, kv_heads: int, tokens: int, device) -> torch.Tensor:
+    """exp(a sin(2 pi t / P + phi)) per (kv, head) row and token, phi uniform per row."""
+    phi = 2.0 * torch.pi * torch.rand(2, kv_heads, 1, 1, generator=g, device=device)
+    t = torch.arange(tokens, device=device, dtype=torch.float32).view(1, 1, tokens, 1)
+    return torch.exp(DRIFT_AMPLITUDE * torch.sin(2.0 * torch.pi * t / DRIFT_PERIOD + phi))
+
+
 def _slab(w: Workload, s_layer: torch.Tensor, tokens: int, seed: int, device):
     """One layer: x bits and mu for [2, H, tokens, D]."""
     g = _gen(seed, device)
     shape = (2, w.kv_heads, tokens, w.head_dim)
     sc = s_layer.to(device).view(2, w.kv_heads, 1, w.head_dim)
+    if w.mu_kind == "drift":
+        # values and residuals scale together with a drift of the (layer, kv, head) row
+        sc = sc * _drift(g, w.kv_heads, tokens, device)
     x16 = (sc * torch.randn(shape, generator=g, device=device)).to(torch.bfloat16)
     xf = x16.to(torch.float32)
     if w.mu_kind == "fp8block":

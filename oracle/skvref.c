@@ -50,10 +50,12 @@ enum { REF_MU_BF16 = 0, REF_MU_F32 = 1 };
 
 enum { REF_SIGMA_CHANNEL = 0, REF_SIGMA_OCTAVE = 1 };
 
+enum { REF_PHAT_STATIC = 0, REF_PHAT_ADAPTIVE = 1 };
+
 typedef struct {
   int64_t layers, kv_heads, tokens, head_dim;
   int32_t sym_fmt, mu_fmt;
-  int32_t sigma_mode, reserved;
+  int32_t sigma_mode, phat_mode;
 } ref_shape;
 
 /* ---- model geometry ---- */
@@ -169,6 +171,11 @@ float skvref_scale(float sigma) {
 }
 
 static float mu_prime(float mu) { return isfinite(mu) ? mu : 0.0f; }
+
+/* symbol i of a bf16 (u16) or e4m3 (u8) array */
+static uint32_t sym_at_(int fmt, const void *x, int64_t i) {
+  return fmt == REF_SYM_BF16 ? ((const uint16_t *)x)[i] : ((const uint8_t *)x)[i];
+}
 
 /*
  * sigma conditioned on the predictor's magnitude (SKV_SIGMA_OCTAVE).  The
@@ -339,21 +346,134 @@ void skvref_model_ptable(const ref_model *m, uint32_t *A) {
  * so freq = cum_hi - cum_lo >= 1 and the frequencies of all N symbols sum
  * to A(N) + MG = T.  This is q integrated over the bin, in integers.
  */
-void skvref_cum_pair(const ref_model *m, float mu, float s, uint32_t b, uint32_t *clo, uint32_t *chi) {
+/* the same with the p_hat table A given (the adaptive tables below) */
+static void cum_pair_with(const ref_model *m, const uint32_t *A, float mu, float s, uint32_t b,
+                          uint32_t *clo, uint32_t *chi) {
   float lo, hi;
   float mp = mu_prime(mu);
   uint32_t k = skvref_rank(m->fmt, b);
   skvref_bin(m->fmt, b, &lo, &hi);
-  *clo = m->A[k] + skvref_cg(m, u_of(lo, mp, s));
-  *chi = m->A[k + 1] + skvref_cg(m, u_of(hi, mp, s));
+  *clo = A[k] + skvref_cg(m, u_of(lo, mp, s));
+  *chi = A[k + 1] + skvref_cg(m, u_of(hi, mp, s));
+}
+
+void skvref_cum_pair(const ref_model *m, float mu, float s, uint32_t b, uint32_t *clo, uint32_t *chi) {
+  cum_pair_with(m, m->A, mu, s, b, clo, chi);
 }
 
 /* cum(k) for k = 0..N: the lower edge of unrank(k); cum(N) = T. */
-static uint32_t cum_rank(const ref_model *m, float mp, float s, uint32_t k) {
+static uint32_t cum_rank_with(const ref_model *m, const uint32_t *A, float mp, float s, uint32_t k) {
   if (k >= m->N) return m->T;
   float lo, hi;
   skvref_bin(m->fmt, skvref_unrank(m->fmt, k), &lo, &hi);
-  return m->A[k] + skvref_cg(m, u_of(lo, mp, s));
+  return A[k] + skvref_cg(m, u_of(lo, mp, s));
+}
+
+static uint32_t cum_rank(const ref_model *m, float mp, float s, uint32_t k) {
+  return cum_rank_with(m, m->A, mp, s, k);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Adaptive p_hat (phat_mode REF_PHAT_ADAPTIVE; e4m3 symbols only).          */
+/* The online entropy-estimation page ([ENT] "虚拟滑动窗口的设计原理") keeps */
+/* exponentially decayed symbol counts, C_t(s) = alpha C_{t-1}(s) +         */
+/* delta(s, s_t), and estimates P_t = C_t / sum C_t; it keeps one window per */
+/* layer-head ("针对 KV 缓存的局部性优化"), rebuilds the CDF lazily every    */
+/* N_update tokens rather than per symbol ("计算优化技巧"), and starts the   */
+/* counters from a calibrated prior against cold start ("局限性与应对").     */
+/* Reading, in integers, so that both ends build identical tables:          */
+/*   - the window is one chunk: chunks decode independently, so every chunk */
+/*     starts again from the prior;                                         */
+/*   - epoch e of a chunk is its scalars i in [e E, (e+1) E), E =           */
+/*     ADAPT_EPOCH, in memory order i = token * D + channel (32 tokens at   */
+/*     head_dim 128), all 64 lanes together;                                */
+/*   - epoch 0 codes with the static table A; epoch e >= 1 with A_e, the    */
+/*     table of the p_hat construction above applied to counts C_e in rank  */
+/*     order: H(0) = 0, H(k+1) = H(k) + C_e(k) + 1, A_e(k) = k +            */
+/*     floor(Mp H(k) / H(N)), A_e(N) = N + Mp;                              */
+/*   - C_0(k) = floor(ADAPT_PRIOR_WEIGHT (A(k+1) - A(k) - 1) / Mp), the     */
+/*     static table's p_hat counts scaled to a total of about               */
+/*     ADAPT_PRIOR_WEIGHT: the calibrated histogram as the prior, worth two */
+/*     epochs of observations;                                              */
+/*   - C_{e+1}(k) = floor(alpha C_e(k)) + (n_e(k) << ADAPT_OBS_SHIFT),      */
+/*     alpha = 1 - 2^-ADAPT_DECAY_SHIFT, n_e(k) the number of epoch-e       */
+/*     scalars of rank k: the decay is applied once per epoch, the epoch's  */
+/*     observations weigh alike, and a count no longer observed decays to 0 */
+/*     (the +1 of the table keeps its symbol's share above zero).           */
+/* The mixture weights stay 0.95 / 0.03 / 0.02: only p_hat adapts.          */
+/* ------------------------------------------------------------------------ */
+#ifndef ADAPT_EPOCH
+#define ADAPT_EPOCH 4096
+#endif
+#ifndef ADAPT_PRIOR_WEIGHT
+#define ADAPT_PRIOR_WEIGHT 8192
+#endif
+#ifndef ADAPT_OBS_SHIFT
+#define ADAPT_OBS_SHIFT 0
+#endif
+#ifndef ADAPT_DECAY_SHIFT
+#define ADAPT_DECAY_SHIFT 2
+#endif
+
+static void adapt_prior(const ref_model *m, uint32_t *C) {
+  for (uint32_t k = 0; k < m->N; k++)
+    C[k] = m->Mp ? (uint32_t)((uint64_t)ADAPT_PRIOR_WEIGHT * (m->A[k + 1] - m->A[k] - 1u) / m->Mp) : 0u;
+}
+
+static void adapt_rebuild(const ref_model *m, const uint32_t *C, uint32_t *A) {
+  uint64_t Htot = 0;
+  for (uint32_t k = 0; k < m->N; k++) Htot += (uint64_t)C[k] + 1;
+  uint64_t H = 0;
+  for (uint32_t k = 0; k < m->N; k++) {
+    A[k] = k + (uint32_t)((uint64_t)m->Mp * H / Htot);
+    H += (uint64_t)C[k] + 1;
+  }
+  A[m->N] = m->N + m->Mp;
+}
+
+/* C <- floor(alpha C) + (n << ADAPT_OBS_SHIFT) */
+static void adapt_step(const ref_model *m, uint32_t *C, const uint32_t *n) {
+  const uint64_t a = (1u << ADAPT_DECAY_SHIFT) - 1u;
+  for (uint32_t k = 0; k < m->N; k++)
+    C[k] = (uint32_t)(((uint64_t)C[k] * a) >> ADAPT_DECAY_SHIFT) + (n[k] << ADAPT_OBS_SHIFT);
+}
+
+int64_t skvref_adapt_epoch(void) { return ADAPT_EPOCH; }
+
+void skvref_adapt_params(int32_t *out4) {
+  out4[0] = ADAPT_EPOCH; out4[1] = ADAPT_PRIOR_WEIGHT; out4[2] = ADAPT_OBS_SHIFT; out4[3] = ADAPT_DECAY_SHIFT;
+}
+
+/* Every epoch table of a chunk of nsc scalars with symbols x_c (encoder
+   side: all symbols are known).  Returns n_ep tables of N + 1 entries. */
+static uint32_t *adapt_tables(const ref_model *m, const ref_shape *sh, const void *x_c, int64_t nsc, int64_t *n_ep) {
+  int64_t ne = (nsc + ADAPT_EPOCH - 1) / ADAPT_EPOCH;
+  if (ne < 1) ne = 1;
+  uint32_t *T = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(m->N + 1) * (size_t)ne);
+  memcpy(T, m->A, sizeof(uint32_t) * (m->N + 1));
+  uint32_t C[256], n[256];
+  adapt_prior(m, C);
+  for (int64_t e = 0; e + 1 < ne; e++) {
+    memset(n, 0, sizeof(n));
+    for (int64_t i = e * ADAPT_EPOCH; i < (e + 1) * ADAPT_EPOCH && i < nsc; i++)
+      n[skvref_rank(m->fmt, sym_at_(sh->sym_fmt, x_c, i))]++;
+    adapt_step(m, C, n);
+    adapt_rebuild(m, C, T + (size_t)(e + 1) * (m->N + 1));
+  }
+  *n_ep = ne;
+  return T;
+}
+
+/* The p_hat tables a chunk's epochs use, for the test suite: n_ep * (N + 1)
+   entries written to out (at most cap tables); returns the epoch count. */
+int64_t skvref_adapt_tables(const ref_model *m, const ref_shape *sh, const void *x_c, int64_t nsc,
+                            uint32_t *out, int64_t cap) {
+  int64_t ne;
+  uint32_t *T = adapt_tables(m, sh, x_c, nsc, &ne);
+  int64_t k = ne < cap ? ne : cap;
+  memcpy(out, T, sizeof(uint32_t) * (size_t)(m->N + 1) * (size_t)k);
+  free(T);
+  return ne;
 }
 
 void skvref_cum_table(const ref_model *m, float mu, float sigma, uint32_t *cum) {
@@ -464,6 +584,9 @@ static int shape_ok(const ref_shape *sh) {
   if (sh->sym_fmt != REF_SYM_BF16 && sh->sym_fmt != REF_SYM_E4M3) return REF_ERR_ARG;
   if (sh->mu_fmt != REF_MU_BF16 && sh->mu_fmt != REF_MU_F32) return REF_ERR_ARG;
   if (sh->sigma_mode != REF_SIGMA_CHANNEL && sh->sigma_mode != REF_SIGMA_OCTAVE) return REF_ERR_ARG;
+  if (sh->phat_mode != REF_PHAT_STATIC && sh->phat_mode != REF_PHAT_ADAPTIVE) return REF_ERR_ARG;
+  /* adaptive p_hat keeps a count per symbol in each chunk's window: e4m3 only */
+  if (sh->phat_mode == REF_PHAT_ADAPTIVE && sh->sym_fmt != REF_SYM_E4M3) return REF_ERR_UNSUPPORTED;
   /* head_dim a power of two from 8 to 512 (a multiple of 8 dividing 512) */
   if (sh->head_dim % 8 != 0 || 512 % sh->head_dim != 0) return REF_ERR_UNSUPPORTED;
   return REF_OK;
@@ -574,19 +697,24 @@ uint64_t skvref_encode_chunk(const ref_model *m, const ref_shape *sh, int64_t ch
   size_t lane_cap = (size_t)(3 * 4 * D + 8);
   uint8_t *lane_buf = (uint8_t *)malloc(lane_cap * LANES);
   uint64_t lens[LANES];
+  int adaptive = sh->phat_mode == REF_PHAT_ADAPTIVE;
+  int64_t n_ep = 1;
+  uint32_t *tabs = adaptive ? adapt_tables(m, sh, x_c, g.nsc, &n_ep) : NULL;
   for (int lane = 0; lane < LANES; lane++) {
     rc_enc e;
     rc_enc_init(&e, lane_buf + lane_cap * lane, lane_cap);
     for (int64_t i = lane; i < g.nsc; i += LANES) {
       uint32_t b = sym_at(sh->sym_fmt, x_c, i);
       float mu = mu_at(sh->mu_fmt, mu_c, i);
+      const uint32_t *A = adaptive ? tabs + (size_t)(i / ADAPT_EPOCH) * (m->N + 1) : m->A;
       uint32_t clo, chi;
-      skvref_cum_pair(m, mu, scale_at(rs, i % D, mu), b, &clo, &chi);
+      cum_pair_with(m, A, mu, scale_at(rs, i % D, mu), b, &clo, &chi);
       rc_encode(&e, (uint64_t)clo << up, (uint64_t)(chi - clo) << up);
     }
     rc_finish(&e);
     lens[lane] = e.n;
   }
+  free(tabs);
   free(rs);
   uint64_t total = HEADER_BYTES;
   for (int l = 0; l < LANES; l++) total += lens[l];
@@ -638,40 +766,63 @@ int skvref_decode_chunk(const ref_model *m, const ref_shape *sh, int64_t chunk,
     for (int l = 0; l < LANES; l++) lens[l] = 0;  /* read nothing */
   }
   uint64_t mw = common_words(lens);
+  /* every lane's substream, gathered from the chunk layout, and its decoder */
   uint8_t *lane = (uint8_t *)malloc((size_t)nbytes + 1);
-  for (int l = 0; l < LANES; l++) {
-    for (uint64_t j = 0; j < lens[l]; j++) lane[j] = bytes[lane_byte_pos(lens, mw, l, j)];
-    rc_dec q;
-    rc_dec_init(&q, lane, (size_t)lens[l]);
-    uint64_t shifts = 0;
-    for (int64_t i = l; i < g.nsc; i += LANES) {
-      float mu = mu_at(sh->mu_fmt, mu_c, i);
-      float mp = mu_prime(mu);
-      float sc = scale_at(rs, i % D, mu);
-      uint64_t r = q.range >> 24;
-      uint64_t t = q.d / (r << up);
-      if (t >= m->T) { st = REF_ERR_CORRUPT; t = m->T - 1; }
-      /* the unique k with cum(k) <= t < cum(k+1), by bisection over ranks */
-      uint32_t lo = 0, hi = m->N;
-      while (hi - lo > 1) {
-        uint32_t mid = (lo + hi) / 2;
-        if (cum_rank(m, mp, sc, mid) <= t) lo = mid; else hi = mid;
-      }
-      uint32_t c = cum_rank(m, mp, sc, lo);
-      uint32_t f = cum_rank(m, mp, sc, lo + 1) - c;
-      q.d -= r * ((uint64_t)c << up);
-      q.range = r * ((uint64_t)f << up);
-      while (q.range < TOP40) {
-        q.d = ((q.d << 8) | rc_byte(&q)) & W48;
-        q.range <<= 8;
-        shifts++;
-      }
-      uint32_t b = skvref_unrank(m->fmt, lo);
-      if (sh->sym_fmt == REF_SYM_BF16) ((uint16_t *)x_out_c)[i] = (uint16_t)b;
-      else ((uint8_t *)x_out_c)[i] = (uint8_t)b;
-    }
-    if (lens[l] == 0 || shifts + 1 != lens[l]) st = REF_ERR_CORRUPT;
+  rc_dec q[LANES];
+  uint64_t shifts[LANES];
+  for (int l = 0, p = 0; l < LANES; p += (int)lens[l], l++) {
+    for (uint64_t j = 0; j < lens[l]; j++) lane[p + j] = bytes[lane_byte_pos(lens, mw, l, j)];
+    rc_dec_init(&q[l], lane + p, (size_t)lens[l]);
+    shifts[l] = 0;
   }
+  /* Epoch by epoch, every lane: an adaptive epoch table needs all lanes'
+     symbols of the epochs before it.  With a static p_hat every epoch uses
+     A, and the order is immaterial. */
+  int adaptive = sh->phat_mode == REF_PHAT_ADAPTIVE;
+  uint32_t *At = (uint32_t *)malloc(sizeof(uint32_t) * (m->N + 1));
+  memcpy(At, m->A, sizeof(uint32_t) * (m->N + 1));
+  uint32_t C[256], n[256];
+  if (adaptive) adapt_prior(m, C);
+  for (int64_t e0 = 0; e0 < g.nsc; e0 += ADAPT_EPOCH) {
+    int64_t e1 = e0 + ADAPT_EPOCH < g.nsc ? e0 + ADAPT_EPOCH : g.nsc;
+    memset(n, 0, sizeof(n));
+    for (int l = 0; l < LANES; l++) {
+      for (int64_t i = e0 + ((l - e0 % LANES) + LANES) % LANES; i < e1; i += LANES) {
+        float mu = mu_at(sh->mu_fmt, mu_c, i);
+        float mp = mu_prime(mu);
+        float sc = scale_at(rs, i % D, mu);
+        uint64_t r = q[l].range >> 24;
+        uint64_t t = q[l].d / (r << up);
+        if (t >= m->T) { st = REF_ERR_CORRUPT; t = m->T - 1; }
+        /* the unique k with cum(k) <= t < cum(k+1), by bisection over ranks */
+        uint32_t lo = 0, hi = m->N;
+        while (hi - lo > 1) {
+          uint32_t mid = (lo + hi) / 2;
+          if (cum_rank_with(m, At, mp, sc, mid) <= t) lo = mid; else hi = mid;
+        }
+        uint32_t c = cum_rank_with(m, At, mp, sc, lo);
+        uint32_t f = cum_rank_with(m, At, mp, sc, lo + 1) - c;
+        q[l].d -= r * ((uint64_t)c << up);
+        q[l].range = r * ((uint64_t)f << up);
+        while (q[l].range < TOP40) {
+          q[l].d = ((q[l].d << 8) | rc_byte(&q[l])) & W48;
+          q[l].range <<= 8;
+          shifts[l]++;
+        }
+        uint32_t b = skvref_unrank(m->fmt, lo);
+        if (sh->sym_fmt == REF_SYM_BF16) ((uint16_t *)x_out_c)[i] = (uint16_t)b;
+        else ((uint8_t *)x_out_c)[i] = (uint8_t)b;
+        if (adaptive) n[lo]++;  /* adaptive mode is e4m3 only: lo < 256 */
+      }
+    }
+    if (adaptive && e1 < g.nsc) {
+      adapt_step(m, C, n);
+      adapt_rebuild(m, C, At);
+    }
+  }
+  for (int l = 0; l < LANES; l++)
+    if (lens[l] == 0 || shifts[l] + 1 != lens[l]) st = REF_ERR_CORRUPT;
+  free(At);
   free(lane);
   free(rs);
   return st;

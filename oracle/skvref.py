@@ -21,6 +21,7 @@ OK, ERR_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLE = 0, 1, 2, 4,
 SYM_BF16, SYM_E4M3 = 0, 1
 MU_BF16, MU_F32 = 0, 1
 SIGMA_CHANNEL, SIGMA_OCTAVE = 0, 1
+PHAT_STATIC, PHAT_ADAPTIVE = 0, 1
 OCTAVES = 8
 OCT_STRIDE = 1 + OCTAVES  # octave-mode sigma table per channel: [sigma_c, sigma_c,0 .. sigma_c,7]
 EXP_BINS = 256
@@ -39,7 +40,7 @@ def build(force: bool = False) -> str:
 class Shape(C.Structure):
     _fields_ = [("layers", C.c_int64), ("kv_heads", C.c_int64), ("tokens", C.c_int64),
                 ("head_dim", C.c_int64), ("sym_fmt", C.c_int32), ("mu_fmt", C.c_int32),
-                ("sigma_mode", C.c_int32), ("reserved", C.c_int32)]
+                ("sigma_mode", C.c_int32), ("phat_mode", C.c_int32)]
 
 
 _lib = None
@@ -80,6 +81,9 @@ def lib():
         L.skvref_calib_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, C.c_int]
         L.skvref_calib_finalize.argtypes = [i64, vp, vp, vp]
         L.skvref_calib_finalize_octave.argtypes = [i64, vp, vp, vp, vp, vp]
+        L.skvref_adapt_tables.restype = i64
+        L.skvref_adapt_tables.argtypes = [vp, vp, vp, i64, vp, i64]
+        L.skvref_adapt_params.argtypes = [vp]
         L.skvref_rc_encode_seq.restype = u64
         L.skvref_rc_encode_seq.argtypes = [vp, vp, i64, vp, u64]
     return _lib
@@ -91,8 +95,15 @@ def _p(a: np.ndarray):
 
 
 def make_shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16,
-               sigma_mode=SIGMA_CHANNEL) -> Shape:
-    return Shape(layers, kv_heads, tokens, head_dim, sym_fmt, mu_fmt, sigma_mode, 0)
+               sigma_mode=SIGMA_CHANNEL, phat_mode=PHAT_STATIC) -> Shape:
+    return Shape(layers, kv_heads, tokens, head_dim, sym_fmt, mu_fmt, sigma_mode, phat_mode)
+
+
+def adapt_params():
+    """(epoch scalars, prior weight, observation shift, decay shift) of the adaptive p_hat."""
+    out = np.zeros(4, dtype=np.int32)
+    lib().skvref_adapt_params(_p(out))
+    return tuple(int(v) for v in out)
 
 
 class Model:
@@ -188,6 +199,14 @@ class Model:
         if st.value != OK:
             raise RuntimeError(f"oracle chunk encode failed (status {st.value})")
         return out[:n].copy()
+
+    def adapt_tables(self, shape: Shape, x_c, nsc: int):
+        """The p_hat table of every epoch of a chunk with symbols x_c (adaptive mode)."""
+        ne = (nsc + adapt_params()[0] - 1) // adapt_params()[0]
+        out = np.zeros((max(ne, 1), self.N + 1), dtype=np.uint32)
+        x_c = np.ascontiguousarray(x_c)
+        n = lib().skvref_adapt_tables(self.ptr, C.byref(shape), _p(x_c), nsc, _p(out), out.shape[0])
+        return out[:n]
 
     def decode_chunk(self, shape: Shape, chunk: int, data, mu_c, sigma_row, out_c):
         data = np.ascontiguousarray(data, dtype=np.uint8)
