@@ -126,7 +126,7 @@ def main():
     print(f"# inputs ready in {time.time() - t0:.1f}s: {w.name}, {w.n_scalars} scalars, {nseq} calibration sequences",
           file=sys.stderr, flush=True)
 
-    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
+    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode, w.phat_mode)
     buf = skv.Buffers(sh, device=dev)
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
@@ -233,7 +233,8 @@ def main():
                    "head_dim": w.head_dim, "symbols": "bf16" if w.sym_fmt == 0 else "e4m3",
                    "mu": "bf16" if w.mu_fmt == 0 else "f32", "n_scalars": n, "calib_seqs": nseq,
                    "calib_tokens": w.calib_tokens, "chunk_tokens": 256, "lanes_per_chunk": 64,
-                   "sigma": "channel x |mu| octave" if w.sigma_mode else "channel"},
+                   "sigma": "channel x |mu| octave" if w.sigma_mode else "channel",
+                   "p_hat": "adaptive (decayed counts per chunk)" if w.phat_mode else "calibrated histogram"},
         "encode_GBps": round(enc_gbps, 3),
         "decode_GBps": round(dec_gbps, 3),
         "encode_ms": round(enc_ms, 4),
@@ -300,7 +301,7 @@ def cpu_baseline(w, x, mu, sigma, hist, buf, seconds):
         ms = mu.reshape(-1, w.tokens, w.head_dim)[:n_rows].cpu().numpy()
         xs = np.ascontiguousarray(xs.view(np.uint16 if w.sym_fmt == 0 else np.uint8))
         ms = np.ascontiguousarray(ms.view(np.uint16) if w.mu_fmt == 0 else ms)
-        shp = (R.make_shape(1, n_rows // 2, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
+        shp = (R.make_shape(1, n_rows // 2, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode, w.phat_mode)
                if n_rows % 2 == 0 else None)
         return xs, ms, shp
 

@@ -56,8 +56,8 @@ extern "C" {
 
 enum skv_status {
   SKV_OK = 0,
-  SKV_ERR_ARG = 1,          /* bad argument (null pointer, bad shape or sigma mode, non-finite or negative sigma) */
-  SKV_ERR_UNSUPPORTED = 2,  /* head_dim not a multiple of 8 dividing 512 */
+  SKV_ERR_ARG = 1,          /* bad argument (null pointer, bad shape, sigma or p_hat mode, non-finite or negative sigma) */
+  SKV_ERR_UNSUPPORTED = 2,  /* head_dim not a multiple of 8 dividing 512; adaptive p_hat with bf16 symbols */
   SKV_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
   SKV_ERR_CAPACITY = 4,     /* the compressed stream does not fit bits_cap */
   SKV_ERR_CORRUPT = 5,      /* the stream does not decode consistently */
@@ -93,6 +93,26 @@ enum skv_sigma_mode { SKV_SIGMA_CHANNEL = 0, SKV_SIGMA_OCTAVE = 1 };
 #define SKV_OCTAVES 8
 #define SKV_OCT_STRIDE (1 + SKV_OCTAVES)
 
+/*
+ * Which p_hat the coder uses.
+ *   SKV_PHAT_STATIC: the calibrated histogram, one table for the whole cache.
+ *   SKV_PHAT_ADAPTIVE (e4m3 symbols only, else SKV_ERR_UNSUPPORTED): decayed
+ *     symbol counts that follow the data, as the online entropy-estimation
+ *     page proposes (decayed counts C_t = alpha C_{t-1} + delta, "虚拟滑动窗口
+ *     的设计原理"; one window per layer-head, "针对 KV 缓存的局部性优化"; a
+ *     calibrated prior against cold start, "局限性与应对").  The window is one
+ *     chunk.  Epoch e of a chunk is its scalars [e E, (e+1) E), E =
+ *     SKV_ADAPT_EPOCH, all lanes together.  Epoch 0 codes with the static
+ *     table; epoch e+1 with the p_hat table built (as the static one is) from
+ *     counts C_{e+1}(k) = floor(alpha C_e(k)) + n_e(k), alpha = 3/4, n_e(k)
+ *     the epoch's scalars of rank k, C_0(k) = floor(SKV_ADAPT_PRIOR_WEIGHT *
+ *     (the static table's p_hat counts of rank k) / Mp).  Only p_hat adapts;
+ *     the mixture weights stay 0.95 / 0.03 / 0.02.
+ */
+enum skv_phat_mode { SKV_PHAT_STATIC = 0, SKV_PHAT_ADAPTIVE = 1 };
+#define SKV_ADAPT_EPOCH 4096
+#define SKV_ADAPT_PRIOR_WEIGHT 8192
+
 typedef struct skv_shape {
   int64_t layers;      /* >= 1 */
   int64_t kv_heads;    /* >= 1 */
@@ -101,7 +121,7 @@ typedef struct skv_shape {
   int32_t sym_fmt;     /* enum skv_sym_fmt: symbols are bf16 (uint16 patterns) or e4m3 (uint8 patterns) */
   int32_t mu_fmt;      /* enum skv_mu_fmt: predictor means are bf16 (uint16 patterns) or fp32 */
   int32_t sigma_mode;  /* enum skv_sigma_mode */
-  int32_t reserved;    /* must be 0 */
+  int32_t phat_mode;   /* enum skv_phat_mode (0: the calibrated histogram) */
 } skv_shape;
 
 /* Human-readable name of a status code (static string, never NULL). */

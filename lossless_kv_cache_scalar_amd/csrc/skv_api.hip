@@ -33,11 +33,13 @@ int make_geo(const skv_shape *sh, Geo &g) {
   if (sh->layers < 1 || sh->kv_heads < 1 || sh->tokens < 1 || sh->head_dim < 1) return SKV_ERR_ARG;
   if (sh->sym_fmt != SKV_SYM_BF16 && sh->sym_fmt != SKV_SYM_E4M3) return SKV_ERR_ARG;
   if (sh->mu_fmt != SKV_MU_BF16 && sh->mu_fmt != SKV_MU_F32) return SKV_ERR_ARG;
-  if ((sh->sigma_mode != SKV_SIGMA_CHANNEL && sh->sigma_mode != SKV_SIGMA_OCTAVE) || sh->reserved != 0)
-    return SKV_ERR_ARG;
+  if (sh->sigma_mode != SKV_SIGMA_CHANNEL && sh->sigma_mode != SKV_SIGMA_OCTAVE) return SKV_ERR_ARG;
+  if (sh->phat_mode != SKV_PHAT_STATIC && sh->phat_mode != SKV_PHAT_ADAPTIVE) return SKV_ERR_ARG;
   // head_dim a power of two from 8 to 512: a lane's channels then repeat with
   // a period dividing kBatch
   if (sh->head_dim % 8 != 0 || 512 % sh->head_dim != 0) return SKV_ERR_UNSUPPORTED;
+  // adaptive p_hat keeps a count per symbol in each chunk's window: e4m3 only
+  if (sh->phat_mode == SKV_PHAT_ADAPTIVE && sh->sym_fmt != SKV_SYM_E4M3) return SKV_ERR_UNSUPPORTED;
   if (sh->layers > (1 << 20) || sh->kv_heads > (1 << 16) || sh->tokens > (int64_t(1) << 32)) return SKV_ERR_ARG;
   g.layers = sh->layers;
   g.heads = sh->kv_heads;
@@ -49,6 +51,7 @@ int make_geo(const skv_shape *sh, Geo &g) {
   g.sym_fmt = sh->sym_fmt;
   g.mu_fmt = sh->mu_fmt;
   g.octave = sh->sigma_mode == SKV_SIGMA_OCTAVE ? 1 : 0;
+  g.adapt = sh->phat_mode == SKV_PHAT_ADAPTIVE ? 1 : 0;
   g.N = sh->sym_fmt == SKV_SYM_BF16 ? 65536u : 256u;
   g.log2T = sh->sym_fmt == SKV_SYM_BF16 ? 24u : 16u;
   // one count per symbol; the rest split 0.98 : 0.02 between the Gaussian
@@ -62,7 +65,7 @@ int make_geo(const skv_shape *sh, Geo &g) {
 }
 
 struct Layout {
-  size_t knots, ptab, a16, abase, aflag, psum, uinv, etab, scale, eref, flags, ctr, scratch, total;
+  size_t knots, ptab, a16, abase, aflag, psum, uinv, etab, prior, scale, eref, flags, ctr, scratch, total;
 };
 
 // The workspace of a call: the model tables, the per-channel scales and the
@@ -79,6 +82,7 @@ Layout layout(const Geo &g, bool enc = true) {
   L.psum = o;  o = align_up(o + sizeof(uint64_t) * 64);
   L.uinv = o;  o = align_up(o + sizeof(float2) * (kNInv + 1));
   L.etab = o;  o = align_up(o + sizeof(float2) * 256);
+  L.prior = o; o = align_up(o + sizeof(uint32_t) * 256);
   L.scale = o; o = align_up(o + sizeof(float2) * (size_t)(g.rows * g.D) * (g.octave ? kOctaves : 1));
   L.eref = o;  o = align_up(o + sizeof(int32_t) * (size_t)(g.octave ? g.rows * g.D : 1));
   L.flags = o; o = align_up(o + (enc ? sizeof(uint64_t) * (size_t)g.n_chunks : 0));
@@ -100,6 +104,7 @@ Workspace carve(const Geo &g, void *base, bool enc = true) {
   w.psum = reinterpret_cast<uint64_t *>(b + L.psum);
   w.uinv = reinterpret_cast<float2 *>(b + L.uinv);
   w.etab = reinterpret_cast<float2 *>(b + L.etab);
+  w.prior = reinterpret_cast<uint32_t *>(b + L.prior);
   w.scale = reinterpret_cast<float2 *>(b + L.scale);
   w.eref = reinterpret_cast<int32_t *>(b + L.eref);
   w.flags = reinterpret_cast<uint64_t *>(b + L.flags);

@@ -22,6 +22,7 @@
 // Stream reads.  Word w of a lane is word 64 w + l of the chunk's interleaved
 // region while w < m, so the lanes' refills read 256 contiguous bytes; each
 // lane keeps its next word in flight.
+#include "skv_adapt.hpp"
 #include "skv_modeldev.hpp"
 
 namespace skv {
@@ -42,6 +43,7 @@ struct DecArgs {
   const int32_t *aflag;
   const float2 *uinv;
   const float2 *etab;
+  const uint32_t *prior;  // adaptive p_hat: the counts a chunk starts from (at rank ^ 0x80)
   const float2 *scale;   // per channel, or per channel and octave
   const int32_t *eref;   // octave mode: per channel octave reference
   float inv_step;  // kNInv / MG
@@ -416,10 +418,16 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   return gs;
 }
 
-template <int SYM, int MU, int PER, int OCT, int TAB>
-__device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs &t, const float2 *uinv) {
+// AD: adaptive p_hat (e4m3): the wave's pair table and counts in `aw`, reset
+// from the block's static pairs and prior at every chunk, rebuilt every epoch
+// from the symbols decoded so far (the encoder rebuilds from the same ones).
+template <int SYM, int MU, int PER, int OCT, int TAB, bool AD>
+__device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs &t0, const float2 *uinv, AdaptLds *aw,
+                                              const uint32_t *s_pairs, const uint32_t *s_prior) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   const Geo &g = a.g;
+  ModelTabs t = t0;
+  if (AD) t.ab = aw->pairs;
   const int lane = threadIdx.x & 63;
   const uint32_t D = (uint32_t)g.D;
   constexpr int kStep = kLanes * kBatch;  // scalars of one batch of the wave
@@ -468,6 +476,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     uint64_t d = (uint64_t)br.take(24) << 24;
     d |= br.take(24);
     uint64_t range = kW48;
+    if (AD) adapt_start(*aw, s_pairs, s_prior, lane);
 
     // ---- symbols: lane l decodes scalars l, l + 64, ... of the chunk; symbol
     // k has channel (l + 64 k) mod D, which repeats with period PER = max(2, D / 64),
@@ -530,18 +539,22 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
         }
       }
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
+      if (AD && b > 0 && b % kAdaptBatches == 0) adapt_rebuild(*aw, g.Mp, lane);  // a new epoch
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const uint32_t gs =
             decode_symbol<SYM, MU, TAB, true>(a, t, uinv, br, d, range, corrupt, OCT ? mj[j] : cur.get(j), cur.v[j],
                                         OCT ? sb[j].x : s[j % PER], OCT ? sb[j].y : sinv[j % PER]);
+        if (AD) adapt_count(*aw, gs);
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
         else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
       }
       cur = nxt;
     }
-    // the last, partial batch of a short chunk: symbol by symbol
+    // the last, partial batch of a short chunk: symbol by symbol (an epoch
+    // boundary can only fall at its start)
+    if (AD && nfull > 0 && nfull % kAdaptBatches == 0 && nsc > nfull * kStep) adapt_rebuild(*aw, g.Mp, lane);
     for (int k = nfull * kBatch; k < nk; ++k) {
       const uint32_t i = (uint32_t)lane + (uint32_t)k * kLanes;
       const int j = k & (kBatch - 1);
@@ -573,6 +586,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
         }
       }
       const uint32_t gs = decode_symbol<SYM, MU, TAB, false>(a, t, uinv, br, d, range, corrupt, m, mraw, sj, sij);
+      if (AD) adapt_count(*aw, gs);
       br.issue();
       if (BF) static_cast<uint16_t *>(x_ch)[i] = (uint16_t)gs;
       else static_cast<uint8_t *>(x_ch)[i] = (uint8_t)gs;
@@ -587,19 +601,29 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
 // then starts below 64 KB, so a table read takes its base as the LDS
 // instruction's immediate offset and its index by one shift (a separate base
 // register costs a three-operand shift-add, twice the issue time of a shift).
-template <bool BF>
+template <bool AD>
+struct DecAdaptBlock {
+  uint32_t prior[256];
+  AdaptLds w[kDecWaves];
+};
+template <>
+struct DecAdaptBlock<false> {};
+
+template <bool BF, bool AD>
 struct DecLds {
   float2 kn[kNKnot];
   float2 ui[kNInv + 1];
   uint32_t ab[BF ? kNWin + 2 : 512];  // (even length: the next table stays 8-byte aligned)
   float2 et[BF ? 1 : 256];
   uint32_t a16w[BF ? kNWin * kWinEntries / 2 : 1];
+  DecAdaptBlock<AD> ad;
 };
 
-template <int SYM, int MU, int PER, int OCT>
+template <int SYM, int MU, int PER, int OCT, int AD>
 __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
-  __shared__ DecLds<BF> lds;
+  static_assert(!(BF && AD), "adaptive p_hat is e4m3 only");
+  __shared__ DecLds<BF, AD != 0> lds;
   float2 *s_kn = lds.kn;
   float2 *s_ui = lds.ui;
   uint32_t *s_a16w = lds.a16w;
@@ -620,10 +644,17 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
     for (int i = threadIdx.x; i < 512; i += kDecBlock) s_ab[i] = a.ptab[((uint32_t)i >> 1 ^ 0x80u) + (i & 1)];
     for (int i = threadIdx.x; i < 256; i += kDecBlock) s_et[i] = a.etab[i];
   }
+  AdaptLds *aw = nullptr;
+  const uint32_t *s_prior = nullptr;
+  if constexpr (AD != 0) {
+    for (int i = threadIdx.x; i < 256; i += kDecBlock) lds.ad.prior[i] = a.prior[i];
+    aw = &lds.ad.w[threadIdx.x >> 6];
+    s_prior = lds.ad.prior;
+  }
   __syncthreads();
   const ModelTabs t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, a.ptab, s_et};
-  if (!BF || win) decode_chunks<SYM, MU, PER, OCT, kTabLdsAll>(a, t, s_ui);
-  else decode_chunks<SYM, MU, PER, OCT, kTabGlobal>(a, t, s_ui);
+  if (!BF || win) decode_chunks<SYM, MU, PER, OCT, kTabLdsAll, AD != 0>(a, t, s_ui, aw, s_ab, s_prior);
+  else decode_chunks<SYM, MU, PER, OCT, kTabGlobal, AD != 0>(a, t, s_ui, aw, s_ab, s_prior);
 }
 
 static int dec_cu_count() {
@@ -637,13 +668,13 @@ static int dec_cu_count() {
   return n;
 }
 
-template <int SYM, int MU>
+template <int SYM, int MU, int AD>
 static void launch_dec_kernel(const DecArgs &a, hipStream_t st) {
   const int64_t need = (a.g.n_chunks + kDecWaves - 1) / kDecWaves;
   const int64_t cus = dec_cu_count();
   const unsigned blocks = (unsigned)(need < cus ? need : cus);
   // the scale period of a lane's symbols: max(2, head_dim / 64); the sigma mode
-#define SKV_DEC(P_, O_) hipLaunchKernelGGL((k_decode<SYM, MU, P_, O_>), dim3(blocks), dim3(kDecBlock), 0, st, a)
+#define SKV_DEC(P_, O_) hipLaunchKernelGGL((k_decode<SYM, MU, P_, O_, AD>), dim3(blocks), dim3(kDecBlock), 0, st, a)
   const int per = a.g.D >= 512 ? 8 : (a.g.D >= 256 ? 4 : 2);
   if (a.g.octave) {
     if (per == 8) SKV_DEC(8, 1); else if (per == 4) SKV_DEC(4, 1); else SKV_DEC(2, 1);
@@ -656,14 +687,17 @@ static void launch_dec_kernel(const DecArgs &a, hipStream_t st) {
 hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes, const uint64_t *offsets,
                          const void *mu, const Workspace &ws, void *x_out, int32_t *status, hipStream_t st) {
   DecArgs a{g, bits, bits_bytes, offsets, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.uinv, ws.etab,
-            ws.scale, ws.eref, (float)kNInv / (float)g.MG, x_out, status, ws.ctr};
+            ws.prior, ws.scale, ws.eref, (float)kNInv / (float)g.MG, x_out, status, ws.ctr};
   timing_mark(kTimeDecode, false, st);
   if (g.sym_fmt == SKV_SYM_BF16) {
-    if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_BF16, SKV_MU_BF16>(a, st);
-    else launch_dec_kernel<SKV_SYM_BF16, SKV_MU_F32>(a, st);
+    if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_BF16, SKV_MU_BF16, 0>(a, st);
+    else launch_dec_kernel<SKV_SYM_BF16, SKV_MU_F32, 0>(a, st);
+  } else if (g.adapt) {
+    if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_E4M3, SKV_MU_BF16, 1>(a, st);
+    else launch_dec_kernel<SKV_SYM_E4M3, SKV_MU_F32, 1>(a, st);
   } else {
-    if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_E4M3, SKV_MU_BF16>(a, st);
-    else launch_dec_kernel<SKV_SYM_E4M3, SKV_MU_F32>(a, st);
+    if (g.mu_fmt == SKV_MU_BF16) launch_dec_kernel<SKV_SYM_E4M3, SKV_MU_BF16, 0>(a, st);
+    else launch_dec_kernel<SKV_SYM_E4M3, SKV_MU_F32, 0>(a, st);
   }
   timing_mark(kTimeDecode, true, st);
   return hipGetLastError();

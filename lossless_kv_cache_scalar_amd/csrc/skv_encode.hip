@@ -17,7 +17,7 @@
 // unfinished chunk never waits), and its wave then writes the chunk (length
 // header, interleaved words, the lanes' remaining bytes, padding) at that
 // offset.
-#include "skv_internal.hpp"
+#include "skv_adapt.hpp"
 
 namespace skv {
 
@@ -33,6 +33,7 @@ struct EncArgs {
   const uint32_t *abase;
   const int32_t *aflag;
   const float2 *etab;
+  const uint32_t *prior;  // adaptive p_hat: the counts a chunk starts from (at rank ^ 0x80)
   const float2 *scale;  // per channel, or per channel and octave
   const int32_t *eref;   // octave mode: per channel octave reference
   uint64_t *flags;  // per chunk: kFlagAgg | size, then kFlagIncl | offset + size
@@ -357,9 +358,14 @@ __device__ __forceinline__ void model_pair(const EncArgs &a, const EncTables &t,
   }
 }
 
-template <int SYM, int MU, int PER, int OCT, bool FAST>
-__device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables &t) {
+// AD: adaptive p_hat (e4m3): the wave's pair table and counts in `aw`, reset
+// from the block's static pairs and prior at every chunk, rebuilt every epoch.
+template <int SYM, int MU, int PER, int OCT, bool FAST, bool AD>
+__device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables &t0, AdaptLds *aw,
+                                              const uint32_t *s_pairs, const uint32_t *s_prior) {
   const Geo &g = a.g;
+  EncTables t = t0;
+  if (AD) t.ab = aw->pairs;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int D = (int)g.D;
@@ -435,6 +441,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 
     LaneCoder cod;
     cod.init(a.scratch + (uint64_t)chunk * kLanes * g.lane_cap, (uint32_t)lane, g.lane_cap / 4);
+    if (AD) adapt_start(*aw, s_pairs, s_prior, lane);
 
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;  // this lane's symbols
     const int nfull = nsc / kStep;                                         // batches every lane fills
@@ -457,6 +464,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
       if (b + 1 < nfull) nxt.load_full(a, base + lane + (int64_t)(b + 1) * kStep);  // in flight meanwhile
+      if (AD && b > 0 && b % kAdaptBatches == 0) adapt_rebuild(*aw, g.Mp, lane);  // a new epoch
       // e4m3: software-pipelined by one symbol, symbol j + 1's model pair (its
       // table reads) issued before symbol j's coder step, whose branches would
       // otherwise keep the reads from starting until the step is done
@@ -482,6 +490,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
           model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), OCT ? sb[j] : s[j % PER], c, f);
           cod.encode(c, f);
         }
+        if (AD) adapt_count(*aw, cur.xs[j]);
       }
       cur = nxt;
       if (OCT) {
@@ -489,11 +498,14 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
         for (int j = 0; j < kBatch; ++j) sb[j] = sbn[j];
       }
     }
-    // the last, partial batch of a short chunk: symbol by symbol
+    // the last, partial batch of a short chunk: symbol by symbol (an epoch
+    // boundary can only fall at its start)
+    if (AD && nfull > 0 && nfull % kAdaptBatches == 0 && nsc > nfull * kStep) adapt_rebuild(*aw, g.Mp, lane);
     for (int k = nfull * kBatch; k < nk; ++k) {
       const int64_t i = base + lane + (int64_t)k * kLanes;
       const int j = k & (kBatch - 1);
       cur.one(a, i, 0);
+      if (AD) adapt_count(*aw, cur.xs[0]);
       float sj;
       if (OCT) {
         int32_t e = er[0];
@@ -553,18 +565,28 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 // then starts below 64 KB, so a table read takes its base as the LDS
 // instruction's immediate offset and its index by one shift (a separate base
 // register costs a three-operand shift-add, twice the issue time of a shift).
-template <bool BF>
+template <bool AD>
+struct AdaptBlock {
+  uint32_t prior[256];
+  AdaptLds w[kEncWaves];
+};
+template <>
+struct AdaptBlock<false> {};
+
+template <bool BF, bool AD>
 struct EncLds {
   float2 kn[kNKnot];
   uint32_t ab[BF ? kNWin + 2 : 512];  // (even length: the next table stays 8-byte aligned)
   float2 et[BF ? 1 : 256];
   uint32_t a16w[BF ? kNWin * kWinEntries / 2 : 1];
+  AdaptBlock<AD> ad;
 };
 
-template <int SYM, int MU, int PER, int OCT>
+template <int SYM, int MU, int PER, int OCT, int AD>
 __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
-  __shared__ EncLds<BF> lds;
+  static_assert(!(BF && AD), "adaptive p_hat is e4m3 only");
+  __shared__ EncLds<BF, AD != 0> lds;
   float2 *s_kn = lds.kn;
   uint32_t *s_a16w = lds.a16w;
   uint32_t *s_ab = lds.ab;
@@ -583,10 +605,17 @@ __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
     for (int i = threadIdx.x; i < 512; i += kEncBlock) s_ab[i] = a.ptab[((uint32_t)i >> 1 ^ 0x80u) + (i & 1)];
     for (int i = threadIdx.x; i < 256; i += kEncBlock) s_et[i] = a.etab[i];
   }
+  AdaptLds *aw = nullptr;
+  const uint32_t *s_prior = nullptr;
+  if constexpr (AD != 0) {
+    for (int i = threadIdx.x; i < 256; i += kEncBlock) lds.ad.prior[i] = a.prior[i];
+    aw = &lds.ad.w[threadIdx.x >> 6];
+    s_prior = lds.ad.prior;
+  }
   __syncthreads();
   const EncTables t{s_kn, reinterpret_cast<const uint16_t *>(s_a16w), s_ab, s_et};
-  if (fast) encode_chunks<SYM, MU, PER, OCT, true>(a, t);
-  else encode_chunks<SYM, MU, PER, OCT, false>(a, t);
+  if (fast) encode_chunks<SYM, MU, PER, OCT, true, AD != 0>(a, t, aw, s_ab, s_prior);
+  else encode_chunks<SYM, MU, PER, OCT, false, AD != 0>(a, t, aw, s_ab, s_prior);
 }
 
 __global__ void k_enc_reset(uint64_t *__restrict__ flags, int64_t n, uint32_t *__restrict__ ctr) {
@@ -606,13 +635,13 @@ static int cu_count() {
   return n;
 }
 
-template <int SYM, int MU>
+template <int SYM, int MU, int AD>
 static void launch_enc_kernel(const EncArgs &a, hipStream_t st) {
   const int64_t need = (a.g.n_chunks + kEncWaves - 1) / kEncWaves;
   const int64_t cus = cu_count();
   const unsigned blocks = (unsigned)(need < cus ? need : cus);
   // the scale period of a lane's symbols: max(2, head_dim / 64); the sigma mode
-#define SKV_ENC(P_, O_) hipLaunchKernelGGL((k_encode<SYM, MU, P_, O_>), dim3(blocks), dim3(kEncBlock), 0, st, a)
+#define SKV_ENC(P_, O_) hipLaunchKernelGGL((k_encode<SYM, MU, P_, O_, AD>), dim3(blocks), dim3(kEncBlock), 0, st, a)
   const int per = a.g.D >= 512 ? 8 : (a.g.D >= 256 ? 4 : 2);
   if (a.g.octave) {
     if (per == 8) SKV_ENC(8, 1); else if (per == 4) SKV_ENC(4, 1); else SKV_ENC(2, 1);
@@ -624,16 +653,19 @@ static void launch_enc_kernel(const EncArgs &a, hipStream_t st) {
 
 hipError_t launch_encode(const Geo &g, const void *x, const void *mu, const Workspace &ws, uint8_t *bits,
                          uint64_t bits_cap, uint64_t *offsets, int32_t *status, hipStream_t st) {
-  EncArgs a{g, x, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.etab, ws.scale, ws.eref, ws.flags, ws.ctr,
-            ws.scratch, bits, bits_cap, offsets, status};
+  EncArgs a{g, x, mu, ws.knots, ws.ptab, ws.a16, ws.abase, ws.aflag, ws.etab, ws.prior, ws.scale, ws.eref, ws.flags,
+            ws.ctr, ws.scratch, bits, bits_cap, offsets, status};
   hipLaunchKernelGGL(k_enc_reset, dim3(256), dim3(256), 0, st, ws.flags, g.n_chunks, ws.ctr);
   timing_mark(kTimeEncode, false, st);
   if (g.sym_fmt == SKV_SYM_BF16) {
-    if (g.mu_fmt == SKV_MU_BF16) launch_enc_kernel<SKV_SYM_BF16, SKV_MU_BF16>(a, st);
-    else launch_enc_kernel<SKV_SYM_BF16, SKV_MU_F32>(a, st);
+    if (g.mu_fmt == SKV_MU_BF16) launch_enc_kernel<SKV_SYM_BF16, SKV_MU_BF16, 0>(a, st);
+    else launch_enc_kernel<SKV_SYM_BF16, SKV_MU_F32, 0>(a, st);
+  } else if (g.adapt) {
+    if (g.mu_fmt == SKV_MU_BF16) launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_BF16, 1>(a, st);
+    else launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_F32, 1>(a, st);
   } else {
-    if (g.mu_fmt == SKV_MU_BF16) launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_BF16>(a, st);
-    else launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_F32>(a, st);
+    if (g.mu_fmt == SKV_MU_BF16) launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_BF16, 0>(a, st);
+    else launch_enc_kernel<SKV_SYM_E4M3, SKV_MU_F32, 0>(a, st);
   }
   timing_mark(kTimeEncode, true, st);
   return hipGetLastError();

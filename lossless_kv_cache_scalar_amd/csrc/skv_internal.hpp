@@ -34,6 +34,12 @@ constexpr int kNWin = 65536 / kWinRanks;
 constexpr int kNInv = 1024;
 constexpr int kOctaves = SKV_OCTAVES;
 constexpr int kExpBins = 256;  // fp32 exponent fields (calibration bins in octave mode)
+// adaptive p_hat (e4m3): epoch length in scalars of a chunk, the prior's
+// weight, alpha = 1 - 2^-kAdaptDecayShift per epoch
+constexpr int kAdaptEpoch = SKV_ADAPT_EPOCH;
+constexpr uint32_t kAdaptPriorWeight = SKV_ADAPT_PRIOR_WEIGHT;
+constexpr int kAdaptDecayShift = 2;
+constexpr int kAdaptBatches = kAdaptEpoch / (64 * 8);  // wave batches of 8 symbols per lane in an epoch
 constexpr uint64_t kW48 = 0xFFFFFFFFFFFFull;
 constexpr uint64_t kTop40 = 1ull << 40;
 
@@ -45,6 +51,7 @@ struct Geo {
   int64_t n_chunks;
   int sym_fmt, mu_fmt;
   int octave;        // sigma per (channel, octave of |mu'|) instead of per channel
+  int adapt;         // adaptive p_hat (e4m3): per-chunk decayed counts, tables rebuilt every epoch
   uint32_t N;        // alphabet: 65536 or 256
   uint32_t log2T;    // 24 or 16
   uint32_t MG, Mp;   // Gaussian-pair and p_hat budgets, MG + Mp = 2^log2T - N
@@ -67,6 +74,7 @@ struct Workspace {
   uint64_t *psum;     // per 1024 ranks: sum of hist + 1 (table build)
   float2 *uinv;       // kNInv + 1: (u, du) at y = m * MG / kNInv
   float2 *etab;       // 256 e4m3 bins (lo, hi), indexed by pattern
+  uint32_t *prior;    // adaptive p_hat: the counts C_0 by rank
   float2 *scale;      // per channel (octave mode: per channel and octave): (s, ~1/s), s = RN32(64 / max(sigma, 2^-100))
   int32_t *eref;      // octave mode, per channel: E(max(sigma_c, 2^-100)) + 1; octave = clamp(E(mu') - eref, 0, 7)
   uint64_t *flags;    // n_chunks published sizes / prefixes (encode)

@@ -158,6 +158,20 @@ __global__ __launch_bounds__(kPtBlock) void k_ptable(const uint64_t *__restrict_
   if (__any(wide) && j == 0) atomicAnd(aflag, 0);
 }
 
+// Adaptive p_hat (e4m3): the prior, the static table's p_hat counts of each
+// rank scaled to the prior weight, C_0(k) = floor(SKV_ADAPT_PRIOR_WEIGHT
+// (A(k+1) - A(k) - 1) / Mp).  Stored already decayed, floor(alpha C_0(k)):
+// the counts a chunk's first epoch adds its symbols to, so that the table of
+// epoch 1 is built from C_1 = floor(alpha C_0) + n_0.  Index k ^ 0x80, as in
+// the kernels' count tables.
+__global__ void k_prior(const uint32_t *__restrict__ A, uint32_t *__restrict__ prior_tix, uint32_t Mp) {
+  const uint32_t k = threadIdx.x;
+  if (k >= 256) return;
+  const uint64_t q = (uint64_t)(A[k + 1] - A[k] - 1u) * kAdaptPriorWeight;
+  const uint32_t c0 = Mp ? (uint32_t)(q / Mp) : 0u;
+  prior_tix[k ^ 0x80u] = (c0 * ((1u << kAdaptDecayShift) - 1u)) >> kAdaptDecayShift;
+}
+
 // ---------------------------------------------------------------- inverse CDF
 // For the decoder's first guess only (every decoded symbol is verified
 // exactly): u at y = m * MG / kNInv on the knot table's piecewise-linear CDF,
@@ -278,6 +292,7 @@ hipError_t launch_model(const Geo &g, const float *sigma, const uint64_t *hist, 
   hipLaunchKernelGGL(k_psums, dim3(pblocks), dim3(kPtBlock), 0, st, hist, ws.psum, ws.aflag, g.N, bf);
   hipLaunchKernelGGL(k_ptable, dim3(pblocks), dim3(kPtBlock), 0, st, hist, ws.psum, ws.ptab, ws.a16, ws.abase,
                      ws.aflag, g.N, g.Mp, bf, status);
+  if (g.adapt) hipLaunchKernelGGL(k_prior, dim3(1), dim3(256), 0, st, ws.ptab, ws.prior, g.Mp);
   hipLaunchKernelGGL(k_uinv, dim3(1), dim3(1024), 0, st, ws.knots, ws.uinv, g.MG);
   if (g.sym_fmt == SKV_SYM_E4M3) hipLaunchKernelGGL(k_etab, dim3(1), dim3(256), 0, st, ws.etab);
   int64_t nch = g.rows * g.D;

@@ -20,6 +20,7 @@ STATIC_SCRATCH_BYTES = 16 << 20  # SKV_STATIC_SCRATCH_BYTES
 SYM_BF16, SYM_E4M3 = 0, 1
 MU_BF16, MU_F32 = 0, 1
 SIGMA_CHANNEL, SIGMA_OCTAVE = 0, 1
+PHAT_STATIC, PHAT_ADAPTIVE = 0, 1
 OCTAVES = 8
 OCT_STRIDE = 1 + OCTAVES
 
@@ -33,7 +34,7 @@ EXPORTS = ["skv_status_string", "skv_num_chunks", "skv_encode_bound", "skv_works
 class SkvShape(C.Structure):
     _fields_ = [("layers", C.c_int64), ("kv_heads", C.c_int64), ("tokens", C.c_int64),
                 ("head_dim", C.c_int64), ("sym_fmt", C.c_int32), ("mu_fmt", C.c_int32),
-                ("sigma_mode", C.c_int32), ("reserved", C.c_int32)]
+                ("sigma_mode", C.c_int32), ("phat_mode", C.c_int32)]
 
 
 class SkvError(RuntimeError):
@@ -76,9 +77,10 @@ def load():
     return L
 
 
-def shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16, sigma_mode=SIGMA_CHANNEL) -> SkvShape:
+def shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16, sigma_mode=SIGMA_CHANNEL,
+          phat_mode=PHAT_STATIC) -> SkvShape:
     return SkvShape(int(layers), int(kv_heads), int(tokens), int(head_dim), int(sym_fmt), int(mu_fmt),
-                    int(sigma_mode), 0)
+                    int(sigma_mode), int(phat_mode))
 
 
 def sigma_floats(sh: SkvShape) -> int:

@@ -28,8 +28,8 @@ def np_mu(t: torch.Tensor, mu_fmt: int) -> np.ndarray:
 
 def shapes(w: synth.Workload, tokens=None):
     t = w.tokens if tokens is None else tokens
-    return (skv.shape(w.layers, w.kv_heads, t, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode),
-            R.make_shape(w.layers, w.kv_heads, t, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode))
+    return (skv.shape(w.layers, w.kv_heads, t, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode, w.phat_mode),
+            R.make_shape(w.layers, w.kv_heads, t, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode, w.phat_mode))
 
 
 def gpu_calibrate(w, seqs):

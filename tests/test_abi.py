@@ -61,16 +61,20 @@ def test_bad_shapes_rejected(lib, bad, code):
 
 
 def test_sigma_mode_checks_and_sizes(lib):
-    """The sigma mode is validated (and the reserved word must be 0); octave
-    mode adds 256 fp64/u64 bin pairs per channel to the calibration state and a
-    scale per channel and octave to the workspace; the chunking is unchanged."""
+    """The sigma and p_hat modes are validated (adaptive p_hat needs e4m3
+    symbols, as in the oracle); octave mode adds 256 fp64/u64 bin pairs per
+    channel to the calibration state and a scale per channel and octave to the
+    workspace; the chunking is unchanged."""
     import ctypes as C
     n = C.c_int64(0)
     bad = skv.shape(1, 1, 256, 64, 0, 0, 2)
     assert lib.skv_num_chunks(C.byref(bad), C.byref(n)) == skv.ERR_ARG
     bad = skv.shape(1, 1, 256, 64)
-    bad.reserved = 1
+    bad.phat_mode = 2
     assert lib.skv_num_chunks(C.byref(bad), C.byref(n)) == skv.ERR_ARG
+    assert lib.skv_num_chunks(C.byref(skv.shape(1, 1, 256, 64, 0, 0, 0, 1)), C.byref(n)) == skv.ERR_UNSUPPORTED
+    assert lib.skv_num_chunks(C.byref(skv.shape(1, 1, 256, 64, 1, 0, 0, 1)), C.byref(n)) == skv.OK
+    assert R.num_chunks(R.make_shape(1, 1, 256, 64, 0, 0, 0, 1)) == -1  # the oracle refuses it too
     ch, oc = skv.shape(2, 4, 300, 128), skv.shape(2, 4, 300, 128, 0, 0, skv.SIGMA_OCTAVE)
     nch = 2 * 2 * 4 * 128
     assert skv.num_chunks(oc) == skv.num_chunks(ch) and skv.encode_bound(oc) == skv.encode_bound(ch)

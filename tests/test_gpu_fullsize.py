@@ -18,7 +18,7 @@ from gpu_util import DEV, ensure_built, np_mu, np_sym
 pytestmark = pytest.mark.gpu
 
 NAMES = ["tiny_bf16", "qwen3_0.6b_bf16", "qwen3_0.6b_e4m3", "qwen3_32b_bf16", "qwen3_32b_e4m3_32k", "qwen3_32b_bf16_fp8res",
-         "qwen3_32b_bf16_fp8res_oct"]
+         "qwen3_32b_bf16_fp8res_oct", "qwen3_0.6b_e4m3_drift", "qwen3_0.6b_e4m3_drift_adapt", "qwen3_32b_e4m3_32k_adapt"]
 CALIB_SEQS = 2  # the launch configuration does not depend on the calibration set's size
 ORACLE_THREADS = 16  # the host's CPU share on a one-GPU machine
 
@@ -46,7 +46,7 @@ def test_full_size_whole_stream_equals_oracle(name):
     del seqs
 
     x, mu = synth.generate(w, device=DEV)
-    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
+    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode, w.phat_mode)
     buf = skv.Buffers(sh, device=DEV)
     buf.encode(x, mu, sigma, hist)
     torch.cuda.synchronize()
@@ -69,7 +69,7 @@ def test_full_size_whole_stream_equals_oracle(name):
     del x, mu, buf
     torch.cuda.empty_cache()
     model = R.Model(w.sym_fmt, rhist)
-    rsh = R.make_shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
+    rsh = R.make_shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode, w.phat_mode)
     t0 = time.perf_counter()
     rbits, roffs = model.encode(rsh, xn, mn, rsigma, nthreads=ORACLE_THREADS)
     print(f"[fullsize] {name}: oracle encode of the whole cache {time.perf_counter() - t0:.1f}s", flush=True)
