@@ -22,6 +22,21 @@ extern "C" const char *skv_status_string(int status) {
   }
 }
 
+namespace skv {
+int device_cu_count() {
+  static std::mutex mu;
+  static int n[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (n[dev] <= 0) {
+    int c = 0;
+    n[dev] = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0 ? c : 256;
+  }
+  return n[dev];
+}
+}  // namespace skv
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -61,6 +76,10 @@ int make_geo(const skv_shape *sh, Geo &g) {
   g.Mp = budget - g.MG;
   // most bytes a lane can emit: 3 per symbol (4 * head_dim symbols) + 1
   g.lane_cap = (uint32_t)((3 * 4 * g.D + 1 + 3) / 4 * 4);
+  // the encoder's persistent grid: one 16-wave block per compute unit at most
+  const int64_t need = (g.n_chunks + 15) / 16;
+  const int64_t cus = device_cu_count();
+  g.enc_blocks = need < cus ? need : cus;
   return SKV_OK;
 }
 
@@ -87,7 +106,9 @@ Layout layout(const Geo &g, bool enc = true) {
   L.eref = o;  o = align_up(o + sizeof(int32_t) * (size_t)(g.octave ? g.rows * g.D : 1));
   L.flags = o; o = align_up(o + (enc ? sizeof(uint64_t) * (size_t)g.n_chunks : 0));
   L.ctr = o;   o = align_up(o + sizeof(uint32_t));
-  L.scratch = o; o = align_up(o + (enc ? (size_t)g.n_chunks * kLanes * g.lane_cap : 0));
+  // two slots per encoder wave: a wave holds at most its current chunk and one
+  // whose offset it is still waiting for
+  L.scratch = o; o = align_up(o + (enc ? (size_t)g.enc_blocks * 16 * 2 * kLanes * g.lane_cap : 0));
   L.total = o;
   return L;
 }

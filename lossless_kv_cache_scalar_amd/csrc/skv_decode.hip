@@ -657,21 +657,10 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   else decode_chunks<SYM, MU, PER, OCT, kTabGlobal, AD != 0>(a, t, s_ui, aw, s_ab, s_prior);
 }
 
-static int dec_cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 template <int SYM, int MU, int AD>
 static void launch_dec_kernel(const DecArgs &a, hipStream_t st) {
   const int64_t need = (a.g.n_chunks + kDecWaves - 1) / kDecWaves;
-  const int64_t cus = dec_cu_count();
+  const int64_t cus = device_cu_count();
   const unsigned blocks = (unsigned)(need < cus ? need : cus);
   // the scale period of a lane's symbols: max(2, head_dim / 64); the sigma mode
 #define SKV_DEC(P_, O_) hipLaunchKernelGGL((k_decode<SYM, MU, P_, O_, AD>), dim3(blocks), dim3(kDecBlock), 0, st, a)

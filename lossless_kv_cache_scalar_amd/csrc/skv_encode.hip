@@ -7,10 +7,12 @@
 // as its own substream, so one wave step reads 64 consecutive scalars of x and
 // of mu.  Lanes load their next 8 symbols while coding the current 8.
 //
-// Each lane writes its substream as whole 32-bit words into the chunk's
-// scratch slot, word w of lane l at word 64 w + l: a wave's stores land side
-// by side, and the first m words of every lane already sit in the stream's
-// interleaved layout.  Chunk ids come from an atomic counter in increasing
+// Each lane writes its substream as whole 32-bit words into a scratch slot,
+// word w of lane l at word 64 w + l: a wave's stores land side by side, and
+// the first m words of every lane already sit in the stream's interleaved
+// layout.  A wave owns two slots and codes its chunks in them by turns: it
+// holds at most the chunk it is coding and one whose offset it is still
+// waiting for, so the scratch scales with the grid, not with the cache.  Chunk ids come from an atomic counter in increasing
 // order; a finished chunk publishes its size, finds its offset by looking back
 // over its predecessors' published sizes and prefixes (a single-pass scan:
 // every chunk it waits for was taken earlier by a running wave, so the lowest
@@ -376,7 +378,12 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
   int64_t pend = -1;
   uint32_t pend_len = 0;
   uint64_t pend_size = 0;
-  auto finalize = [&](int64_t c, uint64_t o0, uint64_t size, uint32_t len) {
+  // this wave's two scratch slots, used by turns
+  const uint64_t wave_gid = (uint64_t)blockIdx.x * kEncWaves + (uint64_t)(threadIdx.x >> 6);
+  uint8_t *const slots = a.scratch + wave_gid * 2 * kLanes * (uint64_t)g.lane_cap;
+  uint32_t taken = 0;  // chunks this wave has started
+  const uint8_t *pend_slot = nullptr;
+  auto finalize = [&](int64_t c, uint64_t o0, uint64_t size, uint32_t len, const uint8_t *slot) {
     if (lane == 0) {
       flag_store(a.flags + c, kFlagIncl | (o0 + size));
       a.offsets[c] = o0;
@@ -389,7 +396,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     // its own loads after a workgroup-scope fence (no cache writeback needed)
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     if (o0 + size <= a.bits_cap)
-      write_chunk(a.bits, o0, size, a.scratch + (uint64_t)c * kLanes * g.lane_cap, len, lane);
+      write_chunk(a.bits, o0, size, slot, len, lane);
   };
   for (;;) {
     uint32_t cid = 0;
@@ -399,7 +406,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
       if (pend >= 0) {
         uint64_t o0;
         if (!look_back(a.flags, pend, lane, o0, kSpinLimit)) set_status(a.status, SKV_ERR_HIP);
-        finalize(pend, o0, pend_size, pend_len);
+        finalize(pend, o0, pend_size, pend_len, pend_slot);
       }
       break;
     }
@@ -440,7 +447,9 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     }
 
     LaneCoder cod;
-    cod.init(a.scratch + (uint64_t)chunk * kLanes * g.lane_cap, (uint32_t)lane, g.lane_cap / 4);
+    uint8_t *slot = slots + (uint64_t)(taken & 1u) * kLanes * g.lane_cap;
+    ++taken;
+    cod.init(slot, (uint32_t)lane, g.lane_cap / 4);
     if (AD) adapt_start(*aw, s_pairs, s_prior, lane);
 
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;  // this lane's symbols
@@ -540,23 +549,24 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     // ---- offsets: publish the size; finish the pending chunk, then this one
     // unless it would have to wait
     if (chunk == 0) {
-      finalize(0, 0, size, nbytes);
+      finalize(0, 0, size, nbytes, slot);
       continue;
     }
     if (lane == 0) flag_store(a.flags + chunk, kFlagAgg | size);
     if (pend >= 0) {
       uint64_t o0;
       if (!look_back(a.flags, pend, lane, o0, kSpinLimit)) set_status(a.status, SKV_ERR_HIP);
-      finalize(pend, o0, pend_size, pend_len);
+      finalize(pend, o0, pend_size, pend_len, pend_slot);
       pend = -1;
     }
     uint64_t o0;
     if (look_back(a.flags, chunk, lane, o0, 0)) {
-      finalize(chunk, o0, size, nbytes);
+      finalize(chunk, o0, size, nbytes, slot);
     } else {
       pend = chunk;
       pend_len = nbytes;
       pend_size = size;
+      pend_slot = slot;
     }
   }
 }
@@ -624,22 +634,11 @@ __global__ void k_enc_reset(uint64_t *__restrict__ flags, int64_t n, uint32_t *_
   if (i0 == 0) *ctr = 0;
 }
 
-static int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 template <int SYM, int MU, int AD>
 static void launch_enc_kernel(const EncArgs &a, hipStream_t st) {
-  const int64_t need = (a.g.n_chunks + kEncWaves - 1) / kEncWaves;
-  const int64_t cus = cu_count();
-  const unsigned blocks = (unsigned)(need < cus ? need : cus);
+  static_assert(kEncWaves == 16, "the workspace holds two scratch slots for each of 16 waves per block");
+  // the grid the workspace's scratch slots were sized for
+  const unsigned blocks = (unsigned)a.g.enc_blocks;
   // the scale period of a lane's symbols: max(2, head_dim / 64); the sigma mode
 #define SKV_ENC(P_, O_) hipLaunchKernelGGL((k_encode<SYM, MU, P_, O_, AD>), dim3(blocks), dim3(kEncBlock), 0, st, a)
   const int per = a.g.D >= 512 ? 8 : (a.g.D >= 256 ? 4 : 2);

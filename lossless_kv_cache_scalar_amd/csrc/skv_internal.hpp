@@ -56,7 +56,11 @@ struct Geo {
   uint32_t log2T;    // 24 or 16
   uint32_t MG, Mp;   // Gaussian-pair and p_hat budgets, MG + Mp = 2^log2T - N
   uint32_t lane_cap; // encoder scratch bytes per lane (multiple of 4)
+  int64_t enc_blocks; // encoder grid: min(chunks / 16 rounded up, compute units); two scratch slots per wave
 };
+
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count();
 
 // Optional per-kernel timing (skv_timing_start .. skv_timing_stop): while it
 // is on, timing_mark records a HIP event on `st` before (end = false) and after
@@ -79,7 +83,7 @@ struct Workspace {
   int32_t *eref;      // octave mode, per channel: E(max(sigma_c, 2^-100)) + 1; octave = clamp(E(mu') - eref, 0, 7)
   uint64_t *flags;    // n_chunks published sizes / prefixes (encode)
   uint32_t *ctr;      // next chunk id (encode)
-  uint8_t *scratch;   // n_chunks * 64 * lane_cap (encode)
+  uint8_t *scratch;   // 2 slots per encoder wave (enc_blocks * 16 waves), 64 * lane_cap bytes each (encode)
 };
 
 // ---- symbol order ----

@@ -111,3 +111,14 @@ def test_decode_static_host_checks(lib):
     huge = skv.shape(2048, 8, 256, 512, 0, 0, skv.SIGMA_OCTAVE)  # 16.8 million channels
     assert lib.skv_decode_static(C.byref(huge), p, 4096, p, p, p, p, p, p, None) == skv.ERR_SCRATCH
     assert skv.status_string(skv.ERR_SCRATCH).startswith("shape needs more")
+
+
+def test_workspace_does_not_grow_with_the_cache(lib):
+    """The encoder's scratch is two slots per wave of its grid (at most one
+    16-wave block per compute unit), so past a few thousand chunks the
+    workspace grows only by the 8-byte published size of each chunk: under
+    1 GB for the 32K-token Qwen3-32B e4m3 cache (4.3e9 scalars)."""
+    a = skv.workspace_size(skv.shape(64, 8, 8192, 128, 1, 0))
+    b = skv.workspace_size(skv.shape(64, 8, 32768, 128, 1, 0))
+    assert b < 1 << 30
+    assert b - a <= 8 * (131072 - 32768) + 4096
