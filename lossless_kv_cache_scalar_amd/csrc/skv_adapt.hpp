@@ -27,7 +27,9 @@ static_assert(kAdaptEpoch % (kLanes * kBatch) == 0, "an epoch is a whole number 
 
 // One wave's adaptive state: the pairs (A(k), A(k + 1)) at 2 (k ^ 0x80) and
 // 2 (k ^ 0x80) + 1 (the static e4m3 table's layout), the counts at k ^ 0x80.
-struct AdaptLds {
+// 16-byte aligned: a pair is read as one 64-bit LDS access, which is slow at
+// an address that is not a multiple of 8.
+struct alignas(16) AdaptLds {
   uint32_t pairs[512];
   uint32_t cnt[256];
 };

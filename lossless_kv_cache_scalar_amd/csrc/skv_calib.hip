@@ -57,34 +57,33 @@ __device__ __forceinline__ double e4m3_value(uint32_t b) {
 
 // One thread per channel: over the call's tokens in order, S += RN(r * r);
 // in octave mode the same square also goes to the bin of mu's exponent field.
+// The loads of kCalUnroll tokens are issued before any of them is added, so a
+// wave keeps that many loads of x and of mu in flight; the additions stay in
+// token order.
+constexpr int kCalUnroll = 8;
+
 template <int SYM, int MU, int OCT>
-__global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, const void *__restrict__ mu,
-                                                    double *__restrict__ S, uint64_t *__restrict__ n,
-                                                    double *__restrict__ So, uint64_t *__restrict__ no, int64_t rows,
-                                                    int64_t tokens, int64_t D) {
-  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= rows * D) return;
-  const int64_t row = c / D, d = c % D;
-  double acc = S[c];
-  uint64_t cnt = n[c];
-  for (int64_t t = 0; t < tokens; ++t) {
-    const int64_t i = (row * tokens + t) * D + d;
+struct CalAcc {
+  double acc;
+  uint64_t cnt;
+  double *So;
+  uint64_t *no;
+  int64_t c;
+  __device__ __forceinline__ void add(uint32_t xb, uint32_t mb) {
     double v;
     bool fin;
     if (SYM == SKV_SYM_BF16) {
-      float f = __uint_as_float((uint32_t)static_cast<const uint16_t *>(x)[i] << 16);
+      const float f = __uint_as_float(xb << 16);
       fin = __builtin_isfinite(f);
       v = (double)f;
     } else {
-      uint32_t b = static_cast<const uint8_t *>(x)[i];
-      fin = (b & 0x7Fu) != 0x7Fu;
-      v = fin ? e4m3_value(b) : 0.0;
+      fin = (xb & 0x7Fu) != 0x7Fu;
+      v = fin ? e4m3_value(xb) : 0.0;
     }
-    if (!fin) continue;
-    float m = MU == SKV_MU_BF16 ? mu_from_bf16(static_cast<const uint16_t *>(mu)[i])
-                                : mu_from_f32(static_cast<const float *>(mu)[i]);
-    double r = v - (double)m;
-    double rr = r * r;
+    if (!fin) return;
+    const float m = MU == SKV_MU_BF16 ? mu_from_bf16(mb) : mu_from_f32(__uint_as_float(mb));
+    const double r = v - (double)m;
+    const double rr = r * r;
     acc = acc + rr;
     ++cnt;
     if (OCT) {
@@ -93,8 +92,39 @@ __global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, 
       no[k] = no[k] + 1;
     }
   }
-  S[c] = acc;
-  n[c] = cnt;
+};
+
+template <int SYM, int MU, int OCT>
+__global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, const void *__restrict__ mu,
+                                                    double *__restrict__ S, uint64_t *__restrict__ n,
+                                                    double *__restrict__ So, uint64_t *__restrict__ no, int64_t rows,
+                                                    int64_t tokens, int64_t D) {
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= rows * D) return;
+  const int64_t row = c / D, d = c % D;
+  CalAcc<SYM, MU, OCT> a{S[c], n[c], So, no, c};
+  auto xload = [&](int64_t i) -> uint32_t {
+    return SYM == SKV_SYM_BF16 ? (uint32_t) static_cast<const uint16_t *>(x)[i]
+                               : (uint32_t) static_cast<const uint8_t *>(x)[i];
+  };
+  auto mload = [&](int64_t i) -> uint32_t {
+    return MU == SKV_MU_BF16 ? (uint32_t) static_cast<const uint16_t *>(mu)[i] : static_cast<const uint32_t *>(mu)[i];
+  };
+  const int64_t i0 = row * tokens * D + d;
+  int64_t t = 0;
+  for (; t + kCalUnroll <= tokens; t += kCalUnroll) {
+    uint32_t xb[kCalUnroll], mb[kCalUnroll];
+#pragma unroll
+    for (int u = 0; u < kCalUnroll; ++u) {
+      xb[u] = xload(i0 + (t + u) * D);
+      mb[u] = mload(i0 + (t + u) * D);
+    }
+#pragma unroll
+    for (int u = 0; u < kCalUnroll; ++u) a.add(xb[u], mb[u]);
+  }
+  for (; t < tokens; ++t) a.add(xload(i0 + t * D), mload(i0 + t * D));
+  S[c] = a.acc;
+  n[c] = a.cnt;
 }
 
 // Histogram: LDS counters for a window of 32768 bins, packed two 16-bit

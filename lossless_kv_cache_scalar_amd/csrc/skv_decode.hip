@@ -540,15 +540,23 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       }
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
       if (AD && b > 0 && b % kAdaptBatches == 0) adapt_rebuild(*aw, g.Mp, lane);  // a new epoch
+      uint32_t packed[AD ? kBatch / 4 : 1];  // the batch's e4m3 symbols, four to a word (adaptive mode)
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const uint32_t gs =
             decode_symbol<SYM, MU, TAB, true>(a, t, uinv, br, d, range, corrupt, OCT ? mj[j] : cur.get(j), cur.v[j],
                                         OCT ? sb[j].x : s[j % PER], OCT ? sb[j].y : sinv[j % PER]);
-        if (AD) adapt_count(*aw, gs);
+        if (AD) packed[j / 4] = (j % 4 == 0 ? 0u : packed[j / 4]) | (gs << (8 * (j % 4)));
         br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
         else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
+      }
+      // the batch's symbols join the epoch's counts after its table reads
+      // (LDS operations complete in order: an atomic among the reads would make
+      // every later read wait for it)
+      if (AD) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) adapt_count(*aw, (packed[j / 4] >> (8 * (j % 4))) & 0xFFu);
       }
       cur = nxt;
     }
@@ -602,7 +610,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
 // instruction's immediate offset and its index by one shift (a separate base
 // register costs a three-operand shift-add, twice the issue time of a shift).
 template <bool AD>
-struct DecAdaptBlock {
+struct alignas(16) DecAdaptBlock {
   uint32_t prior[256];
   AdaptLds w[kDecWaves];
 };
@@ -648,7 +656,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   const uint32_t *s_prior = nullptr;
   if constexpr (AD != 0) {
     for (int i = threadIdx.x; i < 256; i += kDecBlock) lds.ad.prior[i] = a.prior[i];
-    aw = &lds.ad.w[threadIdx.x >> 6];
+    aw = &lds.ad.w[__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))];
     s_prior = lds.ad.prior;
   }
   __syncthreads();

@@ -379,7 +379,9 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
   uint32_t pend_len = 0;
   uint64_t pend_size = 0;
   // this wave's two scratch slots, used by turns
-  const uint64_t wave_gid = (uint64_t)blockIdx.x * kEncWaves + (uint64_t)(threadIdx.x >> 6);
+  // (the wave index read as uniform, so the slot addresses stay in scalar registers)
+  const uint64_t wave_gid =
+      (uint64_t)blockIdx.x * kEncWaves + (uint64_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint8_t *const slots = a.scratch + wave_gid * 2 * kLanes * (uint64_t)g.lane_cap;
   uint32_t taken = 0;  // chunks this wave has started
   const uint8_t *pend_slot = nullptr;
@@ -499,7 +501,13 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
           model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), OCT ? sb[j] : s[j % PER], c, f);
           cod.encode(c, f);
         }
-        if (AD) adapt_count(*aw, cur.xs[j]);
+      }
+      // the batch's symbols join the epoch's counts after its table reads: LDS
+      // operations complete in order, so an atomic among the reads would make
+      // every later read wait for it
+      if (AD) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) adapt_count(*aw, cur.xs[j]);
       }
       cur = nxt;
       if (OCT) {
@@ -576,7 +584,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 // instruction's immediate offset and its index by one shift (a separate base
 // register costs a three-operand shift-add, twice the issue time of a shift).
 template <bool AD>
-struct AdaptBlock {
+struct alignas(16) AdaptBlock {
   uint32_t prior[256];
   AdaptLds w[kEncWaves];
 };
@@ -619,7 +627,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
   const uint32_t *s_prior = nullptr;
   if constexpr (AD != 0) {
     for (int i = threadIdx.x; i < 256; i += kEncBlock) lds.ad.prior[i] = a.prior[i];
-    aw = &lds.ad.w[threadIdx.x >> 6];
+    aw = &lds.ad.w[__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))];
     s_prior = lds.ad.prior;
   }
   __syncthreads();
