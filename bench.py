@@ -51,9 +51,10 @@ def csrc_hash() -> str:
 
 
 def counter_record(kernel: str, workload: str):
-    """The committed rocprofv3 counter record of a kernel, if it was taken on the
-    current kernel sources and on this workload."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    """The committed rocprofv3 counter record of a kernel on a workload
+    (profiles/traffic_<kernel>_<workload>.json), if it was taken on the
+    current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -142,7 +143,8 @@ def main():
         buf.decode(mu, sigma, hist, out, stream=stream)
         torch.cuda.synchronize()
         print(json.dumps({"traffic_probe": w.name, "copy_bytes": 1 << 30, "stream_bytes": buf.stream_bytes(),
-                          "n_scalars": w.n_scalars, "exact": bool(torch.equal(out, x)),
+                          "n_scalars": w.n_scalars, "n_chunks": buf.n_chunks, "sym_bytes": w.sym_bytes,
+                          "mu_bytes": w.mu_bytes, "exact": bool(torch.equal(out, x)),
                           "csrc_hash": csrc_hash()}), flush=True)
         return
 

@@ -22,6 +22,10 @@
 // Stream reads.  Word w of a lane is word 64 w + l of the chunk's interleaved
 // region while w < m, so the lanes' refills read 256 contiguous bytes; each
 // lane keeps its next word in flight.
+//
+// Adaptive p_hat (e4m3): the wave's count and pair tables in LDS follow the
+// decoded symbols and are rebuilt every epoch, exactly where the encoder
+// rebuilt them (skv_adapt.hpp).
 #include "skv_adapt.hpp"
 #include "skv_modeldev.hpp"
 

@@ -12,7 +12,12 @@
 // the first m words of every lane already sit in the stream's interleaved
 // layout.  A wave owns two slots and codes its chunks in them by turns: it
 // holds at most the chunk it is coding and one whose offset it is still
-// waiting for, so the scratch scales with the grid, not with the cache.  Chunk ids come from an atomic counter in increasing
+// waiting for, so the scratch scales with the grid, not with the cache.
+//
+// With the adaptive p_hat (e4m3), each wave also keeps its chunk's symbol
+// counts and p_hat pair table in LDS and rebuilds the table every epoch
+// (skv_adapt.hpp); the decoder rebuilds at the same points from the same
+// symbols.  Chunk ids come from an atomic counter in increasing
 // order; a finished chunk publishes its size, finds its offset by looking back
 // over its predecessors' published sizes and prefixes (a single-pass scan:
 // every chunk it waits for was taken earlier by a running wave, so the lowest
