@@ -55,7 +55,8 @@ def test_adaptive_workloads_reduced(name, mode):
 
 @pytest.mark.parametrize("tokens,head_dim,mu_fmt,mode", [
     (1, 64, 0, 0), (65, 64, 1, 0), (33, 128, 0, 0), (300, 128, 1, 1), (256, 512, 0, 0), (40, 512, 1, 1),
-    (257, 256, 0, 0), (300, 32, 1, 0), (511, 16, 0, 1), (3, 8, 1, 0)])
+    (257, 256, 0, 0), (300, 32, 1, 0), (511, 16, 0, 1), (3, 8, 1, 0), (257, 256, 1, 1), (300, 256, 0, 1),
+    (256, 512, 1, 0), (300, 64, 0, 1)])
 def test_adaptive_ragged_shapes(tokens, head_dim, mu_fmt, mode):
     """65 x 64 and 33 x 128 put an epoch boundary right at the start of the
     last partial batch; 256 x 512 has 32 epochs per chunk."""

@@ -144,16 +144,23 @@ def test_ragged_shapes(tokens, head_dim, sym, mu_fmt):
     assert torch.equal(out.cpu(), x)
 
 
-@pytest.mark.parametrize("tokens,head_dim,sym", [(3, 128, 0), (300, 64, 1), (257, 8, 0), (40, 512, 1), (600, 256, 0)])
-def test_ragged_shapes_octave_mode(tokens, head_dim, sym):
-    """Octave mode on every scale period (head_dim 8 .. 512) and ragged chunks,
-    with a random table (zero, tiny and large sigmas) and non-finite means."""
-    w = synth.Workload("ragged_oct", 1, 2, 3, head_dim, tokens, sym, 0, 0.02, 1, 64, "mixture", 1)
+@pytest.mark.parametrize("tokens,head_dim,sym,mu_fmt", [
+    (3, 128, 0, 0), (300, 64, 1, 0), (257, 8, 0, 0), (40, 512, 1, 0), (600, 256, 0, 0),
+    (40, 512, 0, 0), (257, 256, 1, 0), (40, 512, 0, 1), (257, 256, 1, 1), (300, 256, 0, 1), (40, 512, 1, 1)])
+def test_ragged_shapes_octave_mode(tokens, head_dim, sym, mu_fmt):
+    """Octave mode on every scale period (head_dim 8 .. 512), both symbol and
+    mean formats, and ragged chunks, with a random table (zero, tiny and large
+    sigmas) and non-finite means."""
+    w = synth.Workload("ragged_oct", 1, 2, 3, head_dim, tokens, sym, mu_fmt, 0.02, 1, 64, "mixture", 1)
     rng = np.random.default_rng(tokens + head_dim + 7)
     x, mu = synth.generate(w)
     mu = mu.clone()
-    mu.view(-1)[::97] = 0x7FC0   # NaN means read as 0
-    mu.view(-1)[::89] = -128     # 0xFF80 = -inf
+    if mu_fmt == 0:
+        mu.view(-1)[::97] = 0x7FC0   # NaN means read as 0
+        mu.view(-1)[::89] = -128     # 0xFF80 = -inf
+    else:
+        mu.view(-1)[::97] = float("nan")
+        mu.view(-1)[::89] = float("-inf")
     table = np.exp(rng.uniform(-9, 1, (w.n_channels, R.OCT_STRIDE))).astype(np.float32)
     table[::5, 0] = 0.0
     table[::7, 3] = 0.0
@@ -163,7 +170,7 @@ def test_ragged_shapes_octave_mode(tokens, head_dim, sym):
     bits, offs, out, st_e, st_d = gpu_roundtrip(sh, x.to(DEV), mu.to(DEV), torch.from_numpy(sigma).to(DEV),
                                                 torch.from_numpy(hist.view(np.int64)).to(DEV))
     assert st_e == skv.OK and st_d == skv.OK
-    rbits, roffs = R.Model(sym, hist).encode(rsh, np_sym(x, sym), np_mu(mu, 0), sigma)
+    rbits, roffs = R.Model(sym, hist).encode(rsh, np_sym(x, sym), np_mu(mu, mu_fmt), sigma)
     np.testing.assert_array_equal(offs, roffs)
     np.testing.assert_array_equal(bits, rbits)
     assert torch.equal(out.cpu(), x)
