@@ -21,7 +21,8 @@
 //
 // Stream reads.  Word w of a lane is word 64 w + l of the chunk's interleaved
 // region while w < m, so the lanes' refills read 256 contiguous bytes; each
-// lane keeps its next word in flight.
+// lane keeps its next word in flight.  Refills happen once per batch of 8
+// symbols, with a wave-wide fallback for a lane that runs short within one.
 //
 // Adaptive p_hat (e4m3): the wave's count and pair tables in LDS follow the
 // decoded symbols and are rebuilt every epoch, exactly where the encoder
@@ -57,10 +58,12 @@ struct DecArgs {
 };
 
 // Bits of one lane's substream, most significant first; bytes at or past its
-// length read as 0.  ib holds the bits before word w.  After every symbol,
-// issue() loads the dword(s) that hold word w into (plo, phi), so take() in
-// the next symbol finds them one symbol old: every symbol issues the same
-// memory operations, and the waits stay short.  Words w < m are aligned
+// length read as 0.  ib holds the bits before word w.  Whenever w advances,
+// issue() loads the dword(s) that hold the new word w into (plo, phi), so the
+// next refill finds them in registers.  A full batch starts with top_up(),
+// which leaves every lane at least 32 bits; a symbol takes at most 24, so a
+// lane falls short within a batch only after a run of expensive symbols, and
+// the per-symbol refill is a rare wave-wide branch.  Words w < m are aligned
 // dwords of the interleaved region (no masking); the lane's tail words may
 // straddle dwords and run past its length.
 struct LaneReader {
@@ -86,14 +89,12 @@ struct LaneReader {
         if (4u * w >= len) a0 = 0u;  // nothing left: any dword of the chunk, masked off below
       }
     }
-    // one load for both cases: separate loads per branch would be merged
-    // with a copy that waits for the data
+    // both dwords on every issue: a load on one branch only would make the
+    // compiler wait for it where the branches join
+    uint32_t a1 = a0 + 4u;
+    if (a1 >= csize) a1 = a0;
     plo = *reinterpret_cast<const uint32_t *>(chunk + a0);
-    if (__builtin_expect(!fast, 0)) {
-      uint32_t a1 = a0 + 4u;
-      if (a1 >= csize) a1 = a0;
-      phi = *reinterpret_cast<const uint32_t *>(chunk + a1);
-    }
+    phi = *reinterpret_cast<const uint32_t *>(chunk + a1);
   }
   // renormalisation bytes taken so far (after the 6 priming bytes)
   __device__ __forceinline__ uint32_t renorm_bytes() const { return (32u * w - (uint32_t)nib) / 8u - 6u; }
@@ -122,14 +123,30 @@ struct LaneReader {
     ipw += 256u;
     issue();
   }
+  // word w joins the buffer (nib <= 32)
+  __device__ __forceinline__ void refill() {
+    ib |= (uint64_t)word() << (32 - nib);
+    nib += 32;
+    ++w;
+    ipw += 256u;
+  }
+  // at least n valid bits, n <= 24 (wave-wide: the refill is rare)
+  __device__ __forceinline__ void ensure(uint32_t n) {
+    if (__builtin_expect(__any(nib < (int)n), 0)) {
+      if (nib < (int)n) refill();
+      issue();
+    }
+  }
+  // at least 32 valid bits before a full batch: one word wherever it fits
+  __device__ __forceinline__ void top_up() {
+    if (__any(nib <= 32)) {
+      if (nib <= 32) refill();
+      issue();
+    }
+  }
   // n in {0, 8, 16, 24}
   __device__ __forceinline__ uint32_t take(uint32_t n) {
-    if (nib < (int)n) {  // nib <= 23
-      ib |= (uint64_t)word() << (32 - nib);
-      nib += 32;
-      ++w;
-      ipw += 256u;
-    }
+    ensure(n);
     const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)(ib >> 32), (0u - n) & 31u, n);
     ib <<= n;
     nib -= (int)n;
@@ -138,12 +155,7 @@ struct LaneReader {
   // (x << n) | take(n) for x < 2^(64 - n), as two 64-bit shifts: the high
   // word of x << n, and the high word of (low word of x : next bits) << n
   __device__ __forceinline__ uint64_t shift_in(uint64_t x, uint32_t n) {
-    if (nib < (int)n) {  // nib <= 23
-      ib |= (uint64_t)word() << (32 - nib);
-      nib += 32;
-      ++w;
-      ipw += 256u;
-    }
+    ensure(n);
     const uint64_t lo = (((uint64_t)(uint32_t)x << 32) | (uint32_t)(ib >> 32)) << n;
     const uint64_t r = ((x << n) & 0xFFFFFFFF00000000ull) | (lo >> 32);
     ib <<= n;
@@ -390,11 +402,11 @@ __device__ __forceinline__ void resolve_misses(const ModelTabs &t, bool miss, bo
 // instruction cache.
 template <int SYM, int MU, int TAB, bool FULL>
 __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelTabs &t, const float2 *uinv,
-                                                  LaneReader &br, uint64_t &d, uint64_t &range,
+                                                  LaneReader &br, uint64_t &d, uint32_t &r,
                                                   bool &corrupt, float m, uint32_t mraw, float sj, float sinvj) {
   constexpr bool BF = SYM == SKV_SYM_BF16;
   constexpr int up = BF ? 0 : 8;
-  const uint32_t r = (uint32_t)(range >> 24);
+  __builtin_assume(r < (1u << 24));
   // ---- guess: invert the Gaussian pair's CDF at t - A(k), first with k the
   // rank of mu, then with k the rank of that first guess (the one-count floor
   // makes A(k) grow by one per rank, which matters near zero)
@@ -418,7 +430,7 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   // ---- update and renormalise
   const uint32_t n8 = __builtin_clz((uint32_t)(pf >> 16)) & 24u;  // pf >= r >= 2^16: clz & ~7
   d = br.shift_in(dd, n8);
-  range = pf << n8;
+  r = __builtin_amdgcn_alignbit((uint32_t)(pf >> 32), (uint32_t)pf, 24u - n8);  // (pf << n8) >> 24 < 2^24
   return gs;
 }
 
@@ -479,7 +491,7 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     br.init((uint32_t)lane);
     uint64_t d = (uint64_t)br.take(24) << 24;
     d |= br.take(24);
-    uint64_t range = kW48;
+    uint32_t range = (uint32_t)(kW48 >> 24);
     if (AD) adapt_start(*aw, s_pairs, s_prior, lane);
 
     // ---- symbols: lane l decodes scalars l, l + 64, ... of the chunk; symbol
@@ -545,13 +557,13 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       if (b + 1 < nfull) nxt.load_full(mu_ch, i0 + kStep);  // in flight meanwhile
       if (AD && b > 0 && b % kAdaptBatches == 0) adapt_rebuild(*aw, g.Mp, lane);  // a new epoch
       uint32_t packed[AD ? kBatch / 4 : 1];  // the batch's e4m3 symbols, four to a word (adaptive mode)
+      br.top_up();
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const uint32_t gs =
             decode_symbol<SYM, MU, TAB, true>(a, t, uinv, br, d, range, corrupt, OCT ? mj[j] : cur.get(j), cur.v[j],
                                         OCT ? sb[j].x : s[j % PER], OCT ? sb[j].y : sinv[j % PER]);
         if (AD) packed[j / 4] = (j % 4 == 0 ? 0u : packed[j / 4]) | (gs << (8 * (j % 4)));
-        br.issue();
         if (BF) static_cast<uint16_t *>(x_ch)[i0 + kLanes * j] = (uint16_t)gs;
         else static_cast<uint8_t *>(x_ch)[i0 + kLanes * j] = (uint8_t)gs;
       }
@@ -599,7 +611,6 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
       }
       const uint32_t gs = decode_symbol<SYM, MU, TAB, false>(a, t, uinv, br, d, range, corrupt, m, mraw, sj, sij);
       if (AD) adapt_count(*aw, gs);
-      br.issue();
       if (BF) static_cast<uint16_t *>(x_ch)[i] = (uint16_t)gs;
       else static_cast<uint8_t *>(x_ch)[i] = (uint8_t)gs;
     }

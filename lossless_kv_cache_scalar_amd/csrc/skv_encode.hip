@@ -170,7 +170,7 @@ __device__ __forceinline__ uint64_t mul24(uint32_t a, uint32_t b) {
 // a lane's word w is out[64 w]).
 __device__ __noinline__ uint64_t carry_out(uint64_t acc, int nbits, uint32_t *out, uint32_t nw, uint32_t capw) {
   if (nbits > 0) {
-    const uint64_t mask = (1ull << nbits) - 1ull;
+    const uint64_t mask = nbits >= 64 ? ~0ull : (1ull << nbits) - 1ull;
     const uint64_t v = ((acc & mask) + 1ull) & mask;
     acc = (acc & ~mask) | v;
     if (v != 0) return acc;
@@ -189,7 +189,8 @@ __device__ __noinline__ uint64_t carry_out(uint64_t acc, int nbits, uint32_t *ou
 // 16 bits shifted out of X are the empty pending bytes of the initial state)
 // and leave as whole words, word w at out[64 w].
 struct LaneCoder {
-  uint64_t X, range, acc;
+  uint64_t X, acc;
+  uint32_t r;  // the 48-bit range over 2^24: only these bits enter the products
   int nbits;
   uint32_t nw, capw;
   uint32_t *out;   // the lane's word 0 in the chunk's slot
@@ -198,7 +199,7 @@ struct LaneCoder {
 
   __device__ __forceinline__ void init(uint8_t *chunk_slot, uint32_t lane, uint32_t cap_words) {
     X = 0;
-    range = kW48;
+    r = (uint32_t)(kW48 >> 24);
     acc = 0;
     nbits = -16;
     nw = 0;
@@ -208,23 +209,28 @@ struct LaneCoder {
     off = 4u * lane;
   }
 
-  // Stores the word that starts at bit nbits - 32 of acc once those 32 bits
-  // are complete (a lane completes a word every few symbols, so most lanes of
-  // a store are masked off and the slot sees each word written once).  At most
-  // 3 bytes per symbol plus the flush: the slot (lane_cap) always has room.
-  __device__ __forceinline__ void flush_word() {
-    if (nbits >= 32) {
-      const uint32_t word = (uint32_t)(acc >> (nbits - 32));
-      *reinterpret_cast<uint32_t *>(slot + off) = __builtin_bswap32(word);
-      ++nw;
-      nbits -= 32;
-      off += 4u * kLanes;
+  // Stores the lane's oldest complete word, the one that starts at bit
+  // nbits - 32 of acc (nbits >= 32).  At most 3 bytes per symbol plus the
+  // flush: the slot (lane_cap) always has room.
+  __device__ __forceinline__ void store_word() {
+    const uint32_t word = (uint32_t)(acc >> (nbits - 32));
+    *reinterpret_cast<uint32_t *>(slot + off) = __builtin_bswap32(word);
+    ++nw;
+    nbits -= 32;
+    off += 4u * kLanes;
+  }
+  // Before a full batch: a word from every lane that has one, so that a lane
+  // holds at most 32 bits, and its symbols add at most 24 bits each.  Within
+  // the batch a lane stores again only when acc would overflow (a rare
+  // wave-wide branch); the slot sees each word written once, from one lane.
+  __device__ __forceinline__ void flush_batch() {
+    if (__any(nbits >= 32)) {
+      if (nbits >= 32) store_word();
     }
   }
 
   // c, f on the coder's 2^24 total (f >= 1)
   __device__ __forceinline__ void encode(uint32_t c, uint32_t f) {
-    const uint32_t r = (uint32_t)(range >> 24);  // range < 2^48
     __builtin_assume(r < (1u << 24));
     // the carry out of bit 63 compares the sum with the old X, which the empty
     // asm hides from the optimiser (it would rewrite the test as Xn < r * c and
@@ -243,15 +249,18 @@ struct LaneCoder {
     // bounds it by 24 whatever rg is, so a lane never emits more than 3 bytes
     // per symbol and never outgrows its slot
     const uint32_t n8 = __builtin_clz((uint32_t)(rg >> 16)) & 24u;
+    // room for n8 more bits in acc (nbits + n8 > 64 implies nbits > 40)
+    if (__builtin_expect(__any(nbits + (int)n8 > 64), 0)) {
+      if (nbits + (int)n8 > 64) store_word();
+    }
     if (__builtin_expect(__any(carry), 0)) {
       if (carry) acc = carry_out(acc, nbits, out, nw, capw);
     }
     const uint32_t outb = __builtin_amdgcn_ubfe((uint32_t)(X >> 32), (0u - n8) & 31u, n8);
     X <<= n8;
-    range = rg << n8;
+    r = __builtin_amdgcn_alignbit(rhi, rlo, 24u - n8);
     acc = (acc << n8) | outb;
     nbits += (int)n8;
-    flush_word();
   }
 
   // round low up to a multiple of 2^40, emit the pending bytes and its top byte
@@ -260,9 +269,10 @@ struct LaneCoder {
     const bool carry = Xn < X;
     X = Xn;
     if (carry) acc = carry_out(acc, nbits, out, nw, capw);
+    while (nbits >= 32) store_word();
     acc = (acc << 24) | (X >> 40);
     nbits += 24;
-    flush_word();
+    if (nbits >= 32) store_word();
     if (nbits > 0 && nw < capw) out[nw * kLanes] = __builtin_bswap32((uint32_t)(acc << (32 - nbits)));
     return 4u * nw + (uint32_t)nbits / 8u;
   }
@@ -487,6 +497,7 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
       // (k_encode -1.5..-3% on the e4m3 caches in an A/B run; bf16, with its
       // larger pair, lost 0.4..2.4% to register pressure)
       constexpr bool kPipe = SYM != SKV_SYM_BF16;
+      cod.flush_batch();
       uint32_t c = 0, f = 0;
       if (kPipe) model_pair<SYM, FAST>(a, t, cur.xs[0], cur.mu(0), OCT ? sb[0] : s[0], c, f);
 #pragma unroll
