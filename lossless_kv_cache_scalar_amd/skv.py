@@ -106,6 +106,47 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _fits(t, nbytes: int, what: str):
+    """A tensor argument must be contiguous and hold at least nbytes (the
+    library reads and writes whole arrays through raw pointers); integer
+    addresses pass unchecked, as in C."""
+    if isinstance(t, torch.Tensor):
+        if not t.is_contiguous():
+            raise SkvError(f"{what}: not contiguous")
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise SkvError(f"{what}: {have} bytes, the shape needs {nbytes}")
+
+
+def _offsets(sh: SkvShape, offsets):
+    """offsets holds n_chunks + 1 entries (an invalid shape is left to the
+    library, which returns its status code)."""
+    n = C.c_int64(0)
+    if load().skv_num_chunks(C.byref(sh), C.byref(n)) == OK:
+        _fits(offsets, 8 * (n.value + 1), "offsets")
+
+
+def _state(sh: SkvShape, state):
+    n = C.c_size_t(0)
+    if load().skv_calib_state_size(C.byref(sh), C.byref(n)) == OK:
+        _fits(state, n.value, "state")
+
+
+def _n_scalars(sh: SkvShape) -> int:
+    return sh.layers * 2 * sh.kv_heads * sh.tokens * sh.head_dim
+
+
+def _model_args(sh: SkvShape, mu, sigma, hist):
+    n = _n_scalars(sh)
+    _fits(mu, n * (2 if sh.mu_fmt == MU_BF16 else 4), "mu")
+    _fits(sigma, 4 * sigma_floats(sh), "sigma")
+    _fits(hist, 8 * (65536 if sh.sym_fmt == SYM_BF16 else 256), "hist")
+
+
+def _symbols(sh: SkvShape, x, what: str):
+    _fits(x, _n_scalars(sh) * (2 if sh.sym_fmt == SYM_BF16 else 1), what)
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -138,35 +179,65 @@ def calib_state_size(sh: SkvShape) -> int:
 
 # ---- raw entry points: same names and arguments as skv.h ----
 def calib_reset(state, sh: SkvShape, stream=None) -> int:
+    _state(sh, state)
     return load().skv_calib_reset(_ptr(state), C.byref(sh), _stream(stream))
 
 
 def calib_accumulate(state, seq_shape: SkvShape, x, mu, stream=None) -> int:
+    _state(seq_shape, state)
+    _symbols(seq_shape, x, "x")
+    _fits(mu, _n_scalars(seq_shape) * (2 if seq_shape.mu_fmt == MU_BF16 else 4), "mu")
     return load().skv_calib_accumulate(_ptr(state), C.byref(seq_shape), _ptr(x), _ptr(mu), _stream(stream))
 
 
 def calib_finalize(state, sh: SkvShape, sigma, hist, stream=None) -> int:
+    _state(sh, state)
+    _fits(sigma, 4 * sigma_floats(sh), "sigma")
+    _fits(hist, 8 * (65536 if sh.sym_fmt == SYM_BF16 else 256), "hist")
     return load().skv_calib_finalize(_ptr(state), C.byref(sh), _ptr(sigma), _ptr(hist), _stream(stream))
 
 
 def calibrate(seq_shape: SkvShape, n_seq: int, x, mu, sigma, hist, state, stream=None) -> int:
+    n = _n_scalars(seq_shape) * max(int(n_seq), 0)
+    _fits(x, n * (2 if seq_shape.sym_fmt == SYM_BF16 else 1), "x")
+    _fits(mu, n * (2 if seq_shape.mu_fmt == MU_BF16 else 4), "mu")
+    _fits(sigma, 4 * sigma_floats(seq_shape), "sigma")
+    _fits(hist, 8 * (65536 if seq_shape.sym_fmt == SYM_BF16 else 256), "hist")
+    _state(seq_shape, state)
     return load().skv_calibrate(C.byref(seq_shape), int(n_seq), _ptr(x), _ptr(mu), _ptr(sigma), _ptr(hist),
                                 _ptr(state), _stream(stream))
 
 
 def encode(sh: SkvShape, x, mu, sigma, hist, bits, bits_cap: int, offsets, workspace, workspace_bytes: int,
            status, stream=None) -> int:
+    _symbols(sh, x, "x")
+    _model_args(sh, mu, sigma, hist)
+    _fits(bits, int(bits_cap), "bits")
+    _offsets(sh, offsets)
+    _fits(workspace, int(workspace_bytes), "workspace")
+    _fits(status, 4, "status")
     return load().skv_encode(C.byref(sh), _ptr(x), _ptr(mu), _ptr(sigma), _ptr(hist), _ptr(bits), int(bits_cap),
                              _ptr(offsets), _ptr(workspace), int(workspace_bytes), _ptr(status), _stream(stream))
 
 
 def decode(sh: SkvShape, bits, bits_bytes: int, offsets, mu, sigma, hist, x_out, workspace, workspace_bytes: int,
            status, stream=None) -> int:
+    _fits(bits, int(bits_bytes), "bits")
+    _offsets(sh, offsets)
+    _model_args(sh, mu, sigma, hist)
+    _symbols(sh, x_out, "x_out")
+    _fits(workspace, int(workspace_bytes), "workspace")
+    _fits(status, 4, "status")
     return load().skv_decode(C.byref(sh), _ptr(bits), int(bits_bytes), _ptr(offsets), _ptr(mu), _ptr(sigma), _ptr(hist), _ptr(x_out),
                              _ptr(workspace), int(workspace_bytes), _ptr(status), _stream(stream))
 
 
 def decode_static(sh: SkvShape, bits, bits_bytes: int, offsets, mu, sigma, hist, x_out, status, stream=None) -> int:
+    _fits(bits, int(bits_bytes), "bits")
+    _offsets(sh, offsets)
+    _model_args(sh, mu, sigma, hist)
+    _symbols(sh, x_out, "x_out")
+    _fits(status, 4, "status")
     return load().skv_decode_static(C.byref(sh), _ptr(bits), int(bits_bytes), _ptr(offsets), _ptr(mu), _ptr(sigma),
                                     _ptr(hist), _ptr(x_out), _ptr(status), _stream(stream))
 

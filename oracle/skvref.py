@@ -94,6 +94,15 @@ def _p(a: np.ndarray):
     return a.ctypes.data_as(C.c_void_p)
 
 
+def _sizes(shape: Shape, x, mu, sigma):
+    """The C code reads whole arrays through raw pointers: refuse short ones."""
+    n = shape.layers * 2 * shape.kv_heads * shape.tokens * shape.head_dim
+    nsig = shape.layers * 2 * shape.kv_heads * shape.head_dim * (OCT_STRIDE if shape.sigma_mode == SIGMA_OCTAVE else 1)
+    for name, a, need in (("x", x, n), ("mu", mu, n), ("sigma", sigma, nsig)):
+        if a is not None and np.asarray(a).size < need:
+            raise ValueError(f"{name}: {np.asarray(a).size} elements, the shape needs {need}")
+
+
 def make_shape(layers, kv_heads, tokens, head_dim, sym_fmt=SYM_BF16, mu_fmt=MU_BF16,
                sigma_mode=SIGMA_CHANNEL, phat_mode=PHAT_STATIC) -> Shape:
     return Shape(layers, kv_heads, tokens, head_dim, sym_fmt, mu_fmt, sigma_mode, phat_mode)
@@ -167,6 +176,7 @@ class Model:
 
     # -- whole cache --
     def encode(self, shape: Shape, x, mu, sigma, nthreads=8, cap=None):
+        _sizes(shape, x, mu, sigma)
         L = lib()
         nc = L.skvref_num_chunks(C.byref(shape))
         bound = L.skvref_encode_bound(C.byref(shape)) if cap is None else cap
@@ -179,6 +189,7 @@ class Model:
         return bits[: int(offs[-1])].copy(), offs
 
     def decode(self, shape: Shape, bits, offsets, mu, sigma, nthreads=8):
+        _sizes(shape, None, mu, sigma)
         L = lib()
         out = np.zeros(mu.shape, dtype=np.uint16 if shape.sym_fmt == SYM_BF16 else np.uint8)
         bits = np.ascontiguousarray(bits, dtype=np.uint8)

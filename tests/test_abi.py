@@ -122,3 +122,32 @@ def test_workspace_does_not_grow_with_the_cache(lib):
     b = skv.workspace_size(skv.shape(64, 8, 32768, 128, 1, 0))
     assert b < 1 << 30
     assert b - a <= 8 * (131072 - 32768) + 4096
+
+
+def test_short_arrays_are_refused_before_any_call(lib):
+    """The binding checks each tensor argument against the shape (the library
+    reads whole arrays through raw pointers), and so does the oracle's numpy
+    wrapper: a sigma array for one kv head, given a shape with two, is refused
+    on both sides instead of read past its end."""
+    import numpy as np
+    import torch
+    sh = skv.shape(1, 2, 300, 128)
+    n = 2 * 2 * 300 * 128
+    x = torch.zeros(n, dtype=torch.int16)
+    mu = torch.zeros(n, dtype=torch.int16)
+    hist = torch.zeros(65536, dtype=torch.int64)
+    short = torch.zeros(2 * 128)
+    with pytest.raises(skv.SkvError, match="sigma"):
+        skv.encode(sh, x, mu, short, hist, 0, 0, 0, 0, 0, 0)
+    with pytest.raises(skv.SkvError, match="sigma"):
+        skv.decode(sh, 0, 0, 0, mu, short, hist, x, 0, 0, 0)
+    with pytest.raises(skv.SkvError, match="x_out"):
+        skv.decode_static(sh, 0, 0, 0, mu, torch.zeros(4 * 128), hist, x[: n // 2], 0)
+    with pytest.raises(skv.SkvError, match="mu"):
+        skv.encode(sh, x, mu[:-1], torch.zeros(4 * 128), hist, 0, 0, 0, 0, 0, 0)
+    with pytest.raises(skv.SkvError, match="contiguous"):
+        skv.encode(sh, x.view(2, -1).t(), mu, torch.zeros(4 * 128), hist, 0, 0, 0, 0, 0, 0)
+    rsh = R.make_shape(1, 2, 300, 128)
+    xn = np.zeros(n, dtype=np.uint16)
+    with pytest.raises(ValueError, match="sigma"):
+        R.Model(0, np.ones(65536, dtype=np.uint64)).encode(rsh, xn, xn, np.zeros(2 * 128, dtype=np.float32))

@@ -99,6 +99,9 @@ def test_adaptive_corrupt_payload_status_matches_oracle():
 def test_adaptive_bf16_is_refused():
     sh = skv.shape(1, 1, 256, 64, 0, 0, 0, 1)
     z = torch.zeros(256 * 64 * 2, dtype=torch.int16, device=DEV)
+    sigma = torch.zeros(2 * 64, dtype=torch.float32, device=DEV)
+    hist = torch.zeros(65536, dtype=torch.int64, device=DEV)
+    big = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
     buf_status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    rc = skv.encode(sh, z, z, z, z, z, 1 << 20, z, z, 1 << 20, buf_status)
+    rc = skv.encode(sh, z, z, sigma, hist, big, 1 << 20, big, big, 1 << 20, buf_status)
     assert rc == skv.ERR_UNSUPPORTED

@@ -12,7 +12,10 @@ status words bit-exact):
 * the TABLE status (a histogram whose smoothed total is outside the table's
   domain, a count whose +1 would wrap in 64 bits);
 * the decoder's lane-alone search, which runs only where a short chunk leaves
-  lanes idle and a guess misses (symbols far in the tails of their means).
+  lanes idle and a guess misses (symbols far in the tails of their means);
+* runs of symbols that cost up to 24 bits each, which drain the decoder's bit
+  buffer and fill the encoder's word accumulator within a batch (the coders
+  refill and store once per batch, and mid-batch only on such runs).
 """
 import dataclasses
 
@@ -199,3 +202,39 @@ def test_table_status_matches_oracle(sym, kind):
     bits, offs, out, st_e, st_d = gpu_roundtrip(sh, x.to(DEV), mu.to(DEV), _dev(sigma), _dev(hist))
     assert st_e == skv.ERR_TABLE and st_d == skv.ERR_TABLE
     assert torch.equal(out.cpu(), x)
+
+
+@pytest.mark.parametrize("sym,mu_fmt,p_far", [(0, 0, 0.5), (0, 0, 1.0), (1, 0, 0.5), (1, 1, 1.0), (0, 1, 0.8)])
+def test_expensive_symbol_runs(sym, mu_fmt, p_far):
+    """Symbols far from their means whose bins hold no p_hat mass cost the most
+    a symbol can (frequency 1 of the coder's total); mixed at random with cheap ones, they
+    push the encoder's accumulator to its 64-bit limit and empty the decoder's
+    buffer inside a batch, at varying bit positions, in every lane."""
+    rng = np.random.default_rng(31 + 2 * sym + mu_fmt)
+    tokens, head_dim = 600, 128
+    shape = (1, 2, 2, tokens, head_dim)
+    n = int(np.prod(shape))
+    muf = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    sigma = np.full(4 * head_dim, 1e-4, dtype=np.float32)  # 2 kv heads x K and V
+    far = rng.uniform(size=n) < p_far
+    val = np.where(far, np.ldexp(rng.uniform(1, 2, n), rng.integers(-2, 8, n)) * rng.choice([-1.0, 1.0], n), muf)
+    val = val.astype(np.float32).reshape(shape)
+    if sym == 0:
+        xn = torch.from_numpy(val).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    else:
+        xn = torch.from_numpy(np.clip(val, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    if mu_fmt == 0:
+        mn = torch.from_numpy(muf.reshape(shape)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    else:
+        mn = muf.reshape(shape)
+    # p_hat mass only where no symbol lies: the far symbols keep the one-count floor
+    N = 65536 if sym == 0 else 256
+    hist = np.zeros(N, dtype=np.uint64)
+    hist[rng.integers(0, N, 16)] = 10 ** 6
+    hist[np.unique(xn.reshape(-1).astype(np.int64))] = 0
+    sh = skv.shape(1, 2, tokens, head_dim, sym, mu_fmt)
+    rsh = R.make_shape(1, 2, tokens, head_dim, sym, mu_fmt)
+    bits, offs = _check(sh, rsh, np.ascontiguousarray(xn), np.ascontiguousarray(mn), sigma, hist)
+    # the far scalars did cost about the most a symbol can: log2 of the coder's
+    # total, 24 bits for bf16 and 16 for e4m3
+    assert 8.0 * offs[-1] / n > 0.9 * p_far * (24 if sym == 0 else 16)
