@@ -185,13 +185,13 @@ __device__ __noinline__ uint64_t carry_out(uint64_t acc, int nbits, uint32_t *ou
 
 // One range-coder lane.  X holds the 48-bit window "low" in its low bits and
 // the two most recently emitted bytes above it, so most carries resolve by
-// plain 64-bit addition; emitted bits collect in acc (nbits valid, the first
-// 16 bits shifted out of X are the empty pending bytes of the initial state)
-// and leave as whole words, word w at out[64 w].
+// plain 64-bit addition; emitted bits collect in acc (64 - room of them valid;
+// the first 16 bits shifted out of X are the empty pending bytes of the
+// initial state) and leave as whole words, word w at out[64 w].
 struct LaneCoder {
   uint64_t X, acc;
   uint32_t r;  // the 48-bit range over 2^24: only these bits enter the products
-  int nbits;
+  int room;      // 64 - the valid bits in acc
   uint32_t nw, capw;
   uint32_t *out;   // the lane's word 0 in the chunk's slot
   uint8_t *slot;   // the chunk's slot (the same for the whole wave)
@@ -201,7 +201,7 @@ struct LaneCoder {
     X = 0;
     r = (uint32_t)(kW48 >> 24);
     acc = 0;
-    nbits = -16;
+    room = 80;  // -16 valid bits
     nw = 0;
     capw = cap_words;
     slot = chunk_slot;
@@ -210,13 +210,13 @@ struct LaneCoder {
   }
 
   // Stores the lane's oldest complete word, the one that starts at bit
-  // nbits - 32 of acc (nbits >= 32).  At most 3 bytes per symbol plus the
+  // 32 - room of acc (room <= 32).  At most 3 bytes per symbol plus the
   // flush: the slot (lane_cap) always has room.
   __device__ __forceinline__ void store_word() {
-    const uint32_t word = (uint32_t)(acc >> (nbits - 32));
+    const uint32_t word = (uint32_t)(acc >> (32 - room));
     *reinterpret_cast<uint32_t *>(slot + off) = __builtin_bswap32(word);
     ++nw;
-    nbits -= 32;
+    room += 32;
     off += 4u * kLanes;
   }
   // Before a full batch: a word from every lane that has one, so that a lane
@@ -224,8 +224,8 @@ struct LaneCoder {
   // the batch a lane stores again only when acc would overflow (a rare
   // wave-wide branch); the slot sees each word written once, from one lane.
   __device__ __forceinline__ void flush_batch() {
-    if (__any(nbits >= 32)) {
-      if (nbits >= 32) store_word();
+    if (__any(room <= 32)) {
+      if (room <= 32) store_word();
     }
   }
 
@@ -249,18 +249,19 @@ struct LaneCoder {
     // bounds it by 24 whatever rg is, so a lane never emits more than 3 bytes
     // per symbol and never outgrows its slot
     const uint32_t n8 = __builtin_clz((uint32_t)(rg >> 16)) & 24u;
-    // room for n8 more bits in acc (nbits + n8 > 64 implies nbits > 40)
-    if (__builtin_expect(__any(nbits + (int)n8 > 64), 0)) {
-      if (nbits + (int)n8 > 64) store_word();
+    // room for n8 more bits in acc (n8 > room implies room < 24: a word is complete)
+    if (__builtin_expect(__any((int)n8 > room), 0)) {
+      if ((int)n8 > room) store_word();
     }
     if (__builtin_expect(__any(carry), 0)) {
-      if (carry) acc = carry_out(acc, nbits, out, nw, capw);
+      if (carry) acc = carry_out(acc, 64 - room, out, nw, capw);
     }
-    const uint32_t outb = __builtin_amdgcn_ubfe((uint32_t)(X >> 32), (0u - n8) & 31u, n8);
+    // the top n8 bits of X (width 0 reads as 0 whatever the offset)
+    const uint32_t outb = __builtin_amdgcn_ubfe((uint32_t)(X >> 32), 32u - n8, n8);
     X <<= n8;
     r = __builtin_amdgcn_alignbit(rhi, rlo, 24u - n8);
     acc = (acc << n8) | outb;
-    nbits += (int)n8;
+    room -= (int)n8;
   }
 
   // round low up to a multiple of 2^40, emit the pending bytes and its top byte
@@ -268,11 +269,12 @@ struct LaneCoder {
     const uint64_t Xn = (X + (kTop40 - 1)) & ~(kTop40 - 1);
     const bool carry = Xn < X;
     X = Xn;
-    if (carry) acc = carry_out(acc, nbits, out, nw, capw);
-    while (nbits >= 32) store_word();
+    if (carry) acc = carry_out(acc, 64 - room, out, nw, capw);
+    while (room <= 32) store_word();
     acc = (acc << 24) | (X >> 40);
-    nbits += 24;
-    if (nbits >= 32) store_word();
+    room -= 24;
+    if (room <= 32) store_word();
+    const int nbits = 64 - room;
     if (nbits > 0 && nw < capw) out[nw * kLanes] = __builtin_bswap32((uint32_t)(acc << (32 - nbits)));
     return 4u * nw + (uint32_t)nbits / 8u;
   }
@@ -491,32 +493,25 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
       if (b + 1 < nfull) nxt.load_full(a, base + lane + (int64_t)(b + 1) * kStep);  // in flight meanwhile
       if (AD && b > 0 && b % kAdaptBatches == 0) adapt_rebuild(*aw, g.Mp, lane);  // a new epoch
-      // e4m3: software-pipelined by one symbol, symbol j + 1's model pair (its
-      // table reads) issued before symbol j's coder step, whose branches would
+      // software-pipelined by one symbol: symbol j + 1's model pair (its table
+      // reads) is issued before symbol j's coder step, whose branches would
       // otherwise keep the reads from starting until the step is done
-      // (k_encode -1.5..-3% on the e4m3 caches in an A/B run; bf16, with its
-      // larger pair, lost 0.4..2.4% to register pressure)
-      constexpr bool kPipe = SYM != SKV_SYM_BF16;
+      // (k_encode -1.5..-3% on the e4m3 caches and -1% on bf16 in A/B runs)
       cod.flush_batch();
       uint32_t c = 0, f = 0;
-      if (kPipe) model_pair<SYM, FAST>(a, t, cur.xs[0], cur.mu(0), OCT ? sb[0] : s[0], c, f);
+      model_pair<SYM, FAST>(a, t, cur.xs[0], cur.mu(0), OCT ? sb[0] : s[0], c, f);
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         if (OCT && j == kBatch / 2 && b + 1 < nfull) {
 #pragma unroll
           for (int q = 0; q < kBatch; ++q) sbn[q] = scale_at(nxt.mu(q), q);
         }
-        if (kPipe) {
-          uint32_t cn = 0, fn = 0;
-          if (j + 1 < kBatch)
-            model_pair<SYM, FAST>(a, t, cur.xs[j + 1], cur.mu(j + 1), OCT ? sb[j + 1] : s[(j + 1) % PER], cn, fn);
-          cod.encode(c, f);
-          c = cn;
-          f = fn;
-        } else {
-          model_pair<SYM, FAST>(a, t, cur.xs[j], cur.mu(j), OCT ? sb[j] : s[j % PER], c, f);
-          cod.encode(c, f);
-        }
+        uint32_t cn = 0, fn = 0;
+        if (j + 1 < kBatch)
+          model_pair<SYM, FAST>(a, t, cur.xs[j + 1], cur.mu(j + 1), OCT ? sb[j + 1] : s[(j + 1) % PER], cn, fn);
+        cod.encode(c, f);
+        c = cn;
+        f = fn;
       }
       // the batch's symbols join the epoch's counts after its table reads: LDS
       // operations complete in order, so an atomic among the reads would make
