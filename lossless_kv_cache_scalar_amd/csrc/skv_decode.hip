@@ -529,13 +529,15 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
     void *x_ch = BF ? (void *)(static_cast<uint16_t *>(a.x_out) + base) : (void *)(static_cast<uint8_t *>(a.x_out) + base);
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;
     const int nfull = nsc / kStep;
-    MuBatch<MU> cur, nxt;
+    // two mean buffers used by turns (the next batch loads into the other
+    // one), so no batch is copied from one set of registers to the other
+    MuBatch<MU> mA, mB;
     if (nfull > 0) {
-      cur.load_full(mu_ch, lane);
+      mA.load_full(mu_ch, lane);
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.v[j]));
+      for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(mA.v[j]));
     }
-    for (int b = 0; b < nfull; ++b) {
+    auto batch = [&](int b, MuBatch<MU> &cur, MuBatch<MU> &nxt) __attribute__((always_inline)) {
       const uint32_t i0 = (uint32_t)lane + (uint32_t)b * kStep;
       // this batch's means were loaded one batch ago; wait for them here, once
       // per batch, and not inside the symbols
@@ -574,8 +576,12 @@ __device__ __forceinline__ void decode_chunks(const DecArgs &a, const ModelTabs 
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) adapt_count(*aw, (packed[j / 4] >> (8 * (j % 4))) & 0xFFu);
       }
-      cur = nxt;
+    };
+    for (int b = 0; b < nfull; b += 2) {
+      batch(b, mA, mB);
+      if (b + 1 < nfull) batch(b + 1, mB, mA);
     }
+    MuBatch<MU> &cur = mA;
     // the last, partial batch of a short chunk: symbol by symbol (an epoch
     // boundary can only fall at its start)
     if (AD && nfull > 0 && nfull % kAdaptBatches == 0 && nsc > nfull * kStep) adapt_rebuild(*aw, g.Mp, lane);

@@ -473,20 +473,23 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 
     const int nk = lane < nsc ? (nsc - lane + kLanes - 1) / kLanes : 0;  // this lane's symbols
     const int nfull = nsc / kStep;                                         // batches every lane fills
-    Batch<SYM, MU> cur, nxt;
+    // two batch buffers used by turns (the next batch loads into the other
+    // one), so no batch is copied from one set of registers to the other
+    Batch<SYM, MU> bA, bB;
     // octave mode: a batch's scales depend on its means; they are read half a
     // batch ahead, once the next batch's means have arrived
-    float sb[kBatch], sbn[kBatch];
+    float sA[kBatch], sB[kBatch];
     if (nfull > 0) {
-      cur.load_full(a, base + lane);
+      bA.load_full(a, base + lane);
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(cur.xs[j]), "v"(cur.ms[j]));
+      for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(bA.xs[j]), "v"(bA.ms[j]));
       if (OCT) {
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) sb[j] = scale_at(cur.mu(j), j);
+        for (int j = 0; j < kBatch; ++j) sA[j] = scale_at(bA.mu(j), j);
       }
     }
-    for (int b = 0; b < nfull; ++b) {
+    auto batch = [&](int b, Batch<SYM, MU> &cur, Batch<SYM, MU> &nxt, float (&sb)[kBatch], float (&sbn)[kBatch])
+                     __attribute__((always_inline)) {
       // this batch's symbols and means were loaded one batch ago; wait for
       // them here, once per batch, and not inside the symbols
 #pragma unroll
@@ -520,12 +523,12 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) adapt_count(*aw, cur.xs[j]);
       }
-      cur = nxt;
-      if (OCT) {
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) sb[j] = sbn[j];
-      }
+    };
+    for (int b = 0; b < nfull; b += 2) {
+      batch(b, bA, bB, sA, sB);
+      if (b + 1 < nfull) batch(b + 1, bB, bA, sB, sA);
     }
+    Batch<SYM, MU> &cur = bA;
     // the last, partial batch of a short chunk: symbol by symbol (an epoch
     // boundary can only fall at its start)
     if (AD && nfull > 0 && nfull % kAdaptBatches == 0 && nsc > nfull * kStep) adapt_rebuild(*aw, g.Mp, lane);
