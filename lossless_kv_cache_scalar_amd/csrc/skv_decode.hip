@@ -173,14 +173,14 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return v;
 }
 
-// e4m3 pattern of e, rounded to nearest even with saturation: the hardware
-// conversion (OCP e4m3, which gives NaN beyond 464), on e clamped to +-448.
-// The instruction writes the low 16 bits only: the word starts at zero, and
-// the second operand 0.0 converts to a zero byte.
+// e4m3 pattern of a guessed value e, rounded to nearest even: the hardware
+// conversion (OCP e4m3).  Beyond +-464 it gives a NaN pattern, which is still
+// a symbol: such a guess misses and the exact search finds the answer, so the
+// guesses skip the clamp.  The instruction writes the low 16 bits only: the
+// word starts at zero, and the second operand 0.0 converts to a zero byte.
 __device__ __forceinline__ uint32_t e4m3_rne_bits(float e) {
   uint32_t v = 0;
-  const float c = __builtin_amdgcn_fmed3f(e, -448.0f, 448.0f);
-  asm("v_cvt_pk_fp8_f32 %0, %1, 0" : "+v"(v) : "v"(c));
+  asm("v_cvt_pk_fp8_f32 %0, %1, 0" : "+v"(v) : "v"(e));
   return v;
 }
 

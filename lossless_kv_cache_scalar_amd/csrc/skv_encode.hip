@@ -10,7 +10,8 @@
 // Each lane writes its substream as whole 32-bit words into a scratch slot,
 // word w of lane l at word 64 w + l: a wave's stores land side by side, and
 // the first m words of every lane already sit in the stream's interleaved
-// layout.  A wave owns two slots and codes its chunks in them by turns: it
+// layout.  A lane stores its completed word at the start of each batch of 8
+// symbols, and within a batch only when its 64-bit accumulator would overflow.  A wave owns two slots and codes its chunks in them by turns: it
 // holds at most the chunk it is coding and one whose offset it is still
 // waiting for, so the scratch scales with the grid, not with the cache.
 //
