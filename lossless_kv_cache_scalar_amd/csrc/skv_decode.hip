@@ -259,8 +259,10 @@ __device__ __forceinline__ bool verify(const ModelTabs &t, uint32_t g, float m, 
                                        int up, uint32_t &clo, uint32_t &chi, uint64_t &dd, uint64_t &pf,
                                        bool &below) {
   model_pair<SYM, TAB>(t, g, m, s, clo, chi);
-  const uint64_t plo = mul24(r, clo << up);
-  pf = mul24(r, (chi - clo) << up);
+  // r 2^up times the counts: one 32 x 32-bit multiply-add each (r 2^up < 2^32)
+  const uint32_t ru = r << up;
+  const uint64_t plo = (uint64_t)ru * clo;
+  pf = (uint64_t)ru * (chi - clo);
   dd = d - plo;
   below = d < plo;
   return dd < pf;
