@@ -96,3 +96,23 @@ def test_full_size_whole_stream_equals_oracle(name):
         dec = np.zeros_like(xc)
         got = gbits[int(offs[c]):int(offs[c + 1])]
         assert model.decode_chunk(rsh, c, got, mc, sc, dec) == R.OK and np.array_equal(dec, xc), f"chunk {c}"
+
+
+def test_full_size_encode_is_deterministic():
+    """Chunks go to waves in whatever order the waves reach the chunk counter,
+    and offsets come from the look-back: two encodes of the 32B bf16 cache in
+    the launch configuration bench.py times give the same bytes and offsets."""
+    w = synth.WORKLOADS["qwen3_32b_bf16"]
+    csh = skv.shape(w.layers, w.kv_heads, w.calib_tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode)
+    sigma, hist = skv.calibrate_sequences(csh, [synth.calibration_set(w, 0, device=DEV)], device=DEV)
+    x, mu = synth.generate(w, device=DEV)
+    sh = skv.shape(w.layers, w.kv_heads, w.tokens, w.head_dim, w.sym_fmt, w.mu_fmt, w.sigma_mode, w.phat_mode)
+    a = skv.Buffers(sh, device=DEV)
+    b = skv.Buffers(sh, device=DEV)
+    a.encode(x, mu, sigma, hist)
+    b.encode(x, mu, sigma, hist)
+    torch.cuda.synchronize()
+    assert int(a.status.item()) == skv.OK and int(b.status.item()) == skv.OK
+    n = a.stream_bytes()
+    assert n == b.stream_bytes()
+    assert torch.equal(a.offsets, b.offsets) and torch.equal(a.bits[:n], b.bits[:n])
