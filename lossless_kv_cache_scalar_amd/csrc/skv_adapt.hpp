@@ -26,7 +26,9 @@ namespace skv {
 static_assert(kAdaptEpoch % (kLanes * kBatch) == 0, "an epoch is a whole number of wave batches");
 
 // One wave's adaptive state: the pairs (A(k), A(k + 1)) at 2 (k ^ 0x80) and
-// 2 (k ^ 0x80) + 1 (the static e4m3 table's layout), the counts at k ^ 0x80.
+// 2 (k ^ 0x80) + 1 (the static e4m3 table's layout), the counts at the
+// symbol's pattern (a coded symbol adds to its count with no index arithmetic;
+// only the rebuild maps ranks to patterns).
 // 16-byte aligned: a pair is read as one 64-bit LDS access, which is slow at
 // an address that is not a multiple of 8.
 struct alignas(16) AdaptLds {
@@ -43,13 +45,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // A chunk starts from the static pairs and the decayed prior counts (both in
-// the block's LDS, 512 and 256 words).
+// the block's LDS, 512 and 256 words; the prior at the symbols' patterns).
 __device__ __forceinline__ void adapt_start(AdaptLds &w, const uint32_t *__restrict__ static_pairs,
-                                            const uint32_t *__restrict__ prior_tix, int lane) {
+                                            const uint32_t *__restrict__ prior, int lane) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) w.pairs[lane + 64 * j] = static_pairs[lane + 64 * j];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w.cnt[lane + 64 * j] = prior_tix[lane + 64 * j];
+  for (int j = 0; j < 4; ++j) w.cnt[lane + 64 * j] = prior[lane + 64 * j];
   wave_lds_sync();
 }
 
@@ -71,7 +73,7 @@ __device__ __forceinline__ void adapt_rebuild(AdaptLds &w, uint32_t Mp, int lane
   uint32_t c[4], s = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    c[j] = w.cnt[(uint32_t)(4 * lane + j) ^ 0x80u];
+    c[j] = w.cnt[unrank_e4m3((uint32_t)(4 * lane + j))];
     s += c[j] + 1u;
   }
   uint32_t inc = s;
@@ -94,12 +96,12 @@ __device__ __forceinline__ void adapt_rebuild(AdaptLds &w, uint32_t Mp, int lane
     const uint32_t ti = (uint32_t)(4 * lane + j) ^ 0x80u;
     w.pairs[2 * ti] = A[j];
     w.pairs[2 * ti + 1] = A[j + 1];
-    w.cnt[ti] = (c[j] * ((1u << kAdaptDecayShift) - 1u)) >> kAdaptDecayShift;
+    w.cnt[unrank_e4m3((uint32_t)(4 * lane + j))] = (c[j] * ((1u << kAdaptDecayShift) - 1u)) >> kAdaptDecayShift;
   }
   wave_lds_sync();
 }
 
 // a coded symbol (e4m3 pattern b) joins the counts of the epoch
-__device__ __forceinline__ void adapt_count(AdaptLds &w, uint32_t b) { atomicAdd(&w.cnt[tix_e4m3(b)], 1u); }
+__device__ __forceinline__ void adapt_count(AdaptLds &w, uint32_t b) { atomicAdd(&w.cnt[b & 0xFFu], 1u); }
 
 }  // namespace skv

@@ -48,7 +48,7 @@ struct DecArgs {
   const int32_t *aflag;
   const float2 *uinv;
   const float2 *etab;
-  const uint32_t *prior;  // adaptive p_hat: the counts a chunk starts from (at rank ^ 0x80)
+  const uint32_t *prior;  // adaptive p_hat: the counts a chunk starts from (at the symbols' patterns)
   const float2 *scale;   // per channel, or per channel and octave
   const int32_t *eref;   // octave mode: per channel octave reference
   float inv_step;  // kNInv / MG

@@ -41,7 +41,7 @@ struct EncArgs {
   const uint32_t *abase;
   const int32_t *aflag;
   const float2 *etab;
-  const uint32_t *prior;  // adaptive p_hat: the counts a chunk starts from (at rank ^ 0x80)
+  const uint32_t *prior;  // adaptive p_hat: the counts a chunk starts from (at the symbols' patterns)
   const float2 *scale;  // per channel, or per channel and octave
   const int32_t *eref;   // octave mode: per channel octave reference
   uint64_t *flags;  // per chunk: kFlagAgg | size, then kFlagIncl | offset + size

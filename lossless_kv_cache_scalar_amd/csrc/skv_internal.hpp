@@ -78,7 +78,7 @@ struct Workspace {
   uint64_t *psum;     // per 1024 ranks: sum of hist + 1 (table build)
   float2 *uinv;       // kNInv + 1: (u, du) at y = m * MG / kNInv
   float2 *etab;       // 256 e4m3 bins (lo, hi), indexed by pattern
-  uint32_t *prior;    // adaptive p_hat: the counts C_0 by rank
+  uint32_t *prior;    // adaptive p_hat: the decayed counts C_0, at the symbols' patterns
   float2 *scale;      // per channel (octave mode: per channel and octave): (s, ~1/s), s = RN32(64 / max(sigma, 2^-100))
   int32_t *eref;      // octave mode, per channel: E(max(sigma_c, 2^-100)) + 1; octave = clamp(E(mu') - eref, 0, 7)
   uint64_t *flags;    // n_chunks published sizes / prefixes (encode)

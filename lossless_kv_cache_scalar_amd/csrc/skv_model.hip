@@ -164,12 +164,12 @@ __global__ __launch_bounds__(kPtBlock) void k_ptable(const uint64_t *__restrict_
 // the counts a chunk's first epoch adds its symbols to, so that the table of
 // epoch 1 is built from C_1 = floor(alpha C_0) + n_0.  Index k ^ 0x80, as in
 // the kernels' count tables.
-__global__ void k_prior(const uint32_t *__restrict__ A, uint32_t *__restrict__ prior_tix, uint32_t Mp) {
+__global__ void k_prior(const uint32_t *__restrict__ A, uint32_t *__restrict__ prior, uint32_t Mp) {
   const uint32_t k = threadIdx.x;
   if (k >= 256) return;
   const uint64_t q = (uint64_t)(A[k + 1] - A[k] - 1u) * kAdaptPriorWeight;
   const uint32_t c0 = Mp ? (uint32_t)(q / Mp) : 0u;
-  prior_tix[k ^ 0x80u] = (c0 * ((1u << kAdaptDecayShift) - 1u)) >> kAdaptDecayShift;
+  prior[unrank_e4m3(k)] = (c0 * ((1u << kAdaptDecayShift) - 1u)) >> kAdaptDecayShift;  // at the symbol's pattern
 }
 
 // ---------------------------------------------------------------- inverse CDF
