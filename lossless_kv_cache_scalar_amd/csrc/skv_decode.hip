@@ -2,7 +2,8 @@
 //
 // Persistent grid, one 1024-thread block per CU with the model's tables in
 // LDS (knots 16 KB, the inverse of the Gaussian pair's CDF 8 KB, the bf16 p_hat
-// table 137 KB).  Each wavefront decodes whole chunks, taking their ids from a
+// table 137 KB); the static e4m3 kernels, whose tables take 28 KB, run five
+// 256-thread blocks per CU instead (5 waves per SIMD rather than 4).  Each wavefront decodes whole chunks, taking their ids from a
 // counter (the waves of a SIMD issue at different rates, so fixed shares would
 // leave the fast ones idle); lane l decodes substream l, the chunk's scalars
 // l, l + 64, ...  The model is rebuilt from
@@ -650,8 +651,24 @@ struct DecLds {
   DecAdaptBlock<AD> ad;
 };
 
+// Threads per block: the static e4m3 kernels in channel mode with head_dim
+// up to 256 have 28 KB of LDS tables and fit 5 waves per SIMD in registers,
+// so they run as 256-thread blocks, 5 to a CU; the others keep one 1024-thread
+// block per CU (the bf16 tables fill the LDS, the adaptive kernels keep 16
+// waves' tables beside them, and the octave and 512-channel e4m3 kernels would
+// spill at 96 registers).
+template <int SYM, int PER, int OCT, int AD>
+struct DecBlockOf {
+  static constexpr bool small = SYM != SKV_SYM_BF16 && !AD && !OCT && PER <= 4;
+  static constexpr int value = small ? 256 : kDecBlock;
+  static constexpr int per_cu = small ? 5 : 1;
+};
+
 template <int SYM, int MU, int PER, int OCT, int AD>
-__global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, DecBlockOf<SYM, PER, OCT, AD>::value),
+                          amdgpu_waves_per_eu(DecBlockOf<SYM, PER, OCT, AD>::small ? 5 : 4)))
+void k_decode(DecArgs a) {
+  constexpr int kB = DecBlockOf<SYM, PER, OCT, AD>::value;
   constexpr bool BF = SYM == SKV_SYM_BF16;
   static_assert(!(BF && AD), "adaptive p_hat is e4m3 only");
   __shared__ DecLds<BF, AD != 0> lds;
@@ -662,23 +679,23 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   float2 *s_et = lds.et;
 
   const bool win = BF ? *a.aflag != 0 : true;
-  for (int i = threadIdx.x; i < kNKnot; i += kDecBlock) s_kn[i] = a.knots[i];
-  for (int i = threadIdx.x; i <= kNInv; i += kDecBlock) s_ui[i] = a.uinv[i];
+  for (int i = threadIdx.x; i < kNKnot; i += kB) s_kn[i] = a.knots[i];
+  for (int i = threadIdx.x; i <= kNInv; i += kB) s_ui[i] = a.uinv[i];
   if (BF) {
     if (win) {
       const uint32_t *src = reinterpret_cast<const uint32_t *>(a.a16);
-      for (int i = threadIdx.x; i < kNWin * kWinEntries / 2; i += kDecBlock) s_a16w[i] = src[i];
-      for (int i = threadIdx.x; i <= kNWin; i += kDecBlock) s_ab[i] = a.abase[i];
+      for (int i = threadIdx.x; i < kNWin * kWinEntries / 2; i += kB) s_a16w[i] = src[i];
+      for (int i = threadIdx.x; i <= kNWin; i += kB) s_ab[i] = a.abase[i];
     }
   } else {
     // (A(k), A(k + 1)) side by side at table index k ^ 0x80
-    for (int i = threadIdx.x; i < 512; i += kDecBlock) s_ab[i] = a.ptab[((uint32_t)i >> 1 ^ 0x80u) + (i & 1)];
-    for (int i = threadIdx.x; i < 256; i += kDecBlock) s_et[i] = a.etab[i];
+    for (int i = threadIdx.x; i < 512; i += kB) s_ab[i] = a.ptab[((uint32_t)i >> 1 ^ 0x80u) + (i & 1)];
+    for (int i = threadIdx.x; i < 256; i += kB) s_et[i] = a.etab[i];
   }
   AdaptLds *aw = nullptr;
   const uint32_t *s_prior = nullptr;
   if constexpr (AD != 0) {
-    for (int i = threadIdx.x; i < 256; i += kDecBlock) lds.ad.prior[i] = a.prior[i];
+    for (int i = threadIdx.x; i < 256; i += kB) lds.ad.prior[i] = a.prior[i];
     aw = &lds.ad.w[__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))];
     s_prior = lds.ad.prior;
   }
@@ -688,20 +705,28 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(DecArgs a) {
   else decode_chunks<SYM, MU, PER, OCT, kTabGlobal, AD != 0>(a, t, s_ui, aw, s_ab, s_prior);
 }
 
+template <int SYM, int MU, int PER, int OCT, int AD>
+static void launch_dec_one(const DecArgs &a, hipStream_t st) {
+  using B = DecBlockOf<SYM, PER, OCT, AD>;
+  const int64_t need = (a.g.n_chunks + B::value / 64 - 1) / (B::value / 64);
+  const int64_t slots = device_cu_count() * B::per_cu;
+  const unsigned blocks = (unsigned)(need < slots ? need : slots);
+  hipLaunchKernelGGL((k_decode<SYM, MU, PER, OCT, AD>), dim3(blocks), dim3(B::value), 0, st, a);
+}
+
 template <int SYM, int MU, int AD>
 static void launch_dec_kernel(const DecArgs &a, hipStream_t st) {
-  const int64_t need = (a.g.n_chunks + kDecWaves - 1) / kDecWaves;
-  const int64_t cus = device_cu_count();
-  const unsigned blocks = (unsigned)(need < cus ? need : cus);
   // the scale period of a lane's symbols: max(2, head_dim / 64); the sigma mode
-#define SKV_DEC(P_, O_) hipLaunchKernelGGL((k_decode<SYM, MU, P_, O_, AD>), dim3(blocks), dim3(kDecBlock), 0, st, a)
   const int per = a.g.D >= 512 ? 8 : (a.g.D >= 256 ? 4 : 2);
   if (a.g.octave) {
-    if (per == 8) SKV_DEC(8, 1); else if (per == 4) SKV_DEC(4, 1); else SKV_DEC(2, 1);
+    if (per == 8) launch_dec_one<SYM, MU, 8, 1, AD>(a, st);
+    else if (per == 4) launch_dec_one<SYM, MU, 4, 1, AD>(a, st);
+    else launch_dec_one<SYM, MU, 2, 1, AD>(a, st);
   } else {
-    if (per == 8) SKV_DEC(8, 0); else if (per == 4) SKV_DEC(4, 0); else SKV_DEC(2, 0);
+    if (per == 8) launch_dec_one<SYM, MU, 8, 0, AD>(a, st);
+    else if (per == 4) launch_dec_one<SYM, MU, 4, 0, AD>(a, st);
+    else launch_dec_one<SYM, MU, 2, 0, AD>(a, st);
   }
-#undef SKV_DEC
 }
 
 hipError_t launch_decode(const Geo &g, const uint8_t *bits, uint64_t bits_bytes, const uint64_t *offsets,
