@@ -11,7 +11,8 @@
 // the same sums split by the fp32 exponent field of mu'.
 //
 // State layout: S (fp64 [channels]) | n (u64 [channels]) | hist (u64 [N]),
-// then in octave mode So (fp64 [channels][256]) | no (u64 [channels][256]).
+// then in octave mode So (fp64 [256][channels]) | no (u64 [256][channels]),
+// exponent-major so that a wave's 64 channels read one bin side by side.
 #include "skv_internal.hpp"
 
 namespace skv {
@@ -61,14 +62,45 @@ __device__ __forceinline__ double e4m3_value(uint32_t b) {
 // wave keeps that many loads of x and of mu in flight; the additions stay in
 // token order.
 constexpr int kCalUnroll = 8;
+constexpr int kCalThreads = 256;
+
+// Octave mode: the bins one call touches are cached in LDS. A first pass over
+// the call's means finds the channel's largest exponent field emax; the window
+// holds the kOctWin fields below and up to emax (from field 1) plus field 0
+// (zero and subnormal means). Each window bin is read from the state before
+// the first token and written back after the last, so every bin still adds its
+// squares in token order, and the bin's count is kept as a u32 added to the
+// state's u64 at the end. A mean below 2^-(kOctWin - 1) of the channel's
+// largest updates its bin in global memory directly. (Updating every bin in
+// global memory made each token wait for the previous one's store: 3.2 ms per
+// call of 512 tokens on the 32B geometry.)
+constexpr int kOctWin = 24;
+constexpr int kOctSlots = kOctWin + 1;  // slot kOctWin holds field 0
+
+struct CalOctLds {
+  double s[kOctSlots][kCalThreads];  // [slot][thread]: a wave's 64 lanes read side by side
+  uint32_t n[kOctSlots][kCalThreads];  // a launch covers at most 2^31 tokens
+};
+constexpr int64_t kOctSegTokens = int64_t(1) << 31;
+template <int OCT>
+struct CalLdsOf {
+  using T = CalOctLds;
+};
+template <>
+struct CalLdsOf<0> {
+  using T = uint32_t;  // channel mode uses no LDS
+};
 
 template <int SYM, int MU, int OCT>
 struct CalAcc {
   double acc;
   uint64_t cnt;
+  // octave mode
+  CalOctLds *lds;
+  uint32_t base;  // exponent field of window slot 0
   double *So;
   uint64_t *no;
-  int64_t c;
+  int64_t c, nch;
   __device__ __forceinline__ void add(uint32_t xb, uint32_t mb) {
     double v;
     bool fin;
@@ -87,22 +119,36 @@ struct CalAcc {
     acc = acc + rr;
     ++cnt;
     if (OCT) {
-      const int64_t k = c * kExpBins + ((__float_as_uint(m) >> 23) & 0xFFu);
-      So[k] = So[k] + rr;
-      no[k] = no[k] + 1;
+      const uint32_t e = (__float_as_uint(m) >> 23) & 0xFFu;
+      uint32_t slot = e - base;  // e < base wraps above the window
+      if (slot >= (uint32_t)kOctWin) slot = kOctSlots;
+      if (e == 0) slot = kOctWin;
+      if (slot < (uint32_t)kOctSlots) {
+        double &sv = lds->s[slot][threadIdx.x];
+        sv = sv + rr;
+        __hip_atomic_fetch_add(&lds->n[slot][threadIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        const int64_t k = (int64_t)e * nch + c;
+        So[k] = So[k] + rr;
+        no[k] = no[k] + 1;
+      }
     }
   }
 };
 
 template <int SYM, int MU, int OCT>
-__global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, const void *__restrict__ mu,
-                                                    double *__restrict__ S, uint64_t *__restrict__ n,
-                                                    double *__restrict__ So, uint64_t *__restrict__ no, int64_t rows,
-                                                    int64_t tokens, int64_t D) {
-  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= rows * D) return;
+__global__ __launch_bounds__(kCalThreads) void k_calib_sums(const void *__restrict__ x, const void *__restrict__ mu,
+                                                            double *__restrict__ S, uint64_t *__restrict__ n,
+                                                            double *__restrict__ So, uint64_t *__restrict__ no,
+                                                            int64_t rows, int64_t tokens, int64_t D, int64_t t0,
+                                                            int64_t t1) {
+  // tokens [t0, t1) of the call; only octave mode uses LDS, each thread its
+  // own column of it, so no barrier
+  __shared__ typename CalLdsOf<OCT>::T lds_oct;
+  const int64_t nch = rows * D;
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nch) return;
   const int64_t row = c / D, d = c % D;
-  CalAcc<SYM, MU, OCT> a{S[c], n[c], So, no, c};
   auto xload = [&](int64_t i) -> uint32_t {
     return SYM == SKV_SYM_BF16 ? (uint32_t) static_cast<const uint16_t *>(x)[i]
                                : (uint32_t) static_cast<const uint8_t *>(x)[i];
@@ -110,9 +156,35 @@ __global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, 
   auto mload = [&](int64_t i) -> uint32_t {
     return MU == SKV_MU_BF16 ? (uint32_t) static_cast<const uint16_t *>(mu)[i] : static_cast<const uint32_t *>(mu)[i];
   };
+  auto mexp = [&](uint32_t mb) -> uint32_t {
+    const float m = MU == SKV_MU_BF16 ? mu_from_bf16(mb) : mu_from_f32(__uint_as_float(mb));
+    return (__float_as_uint(m) >> 23) & 0xFFu;
+  };
   const int64_t i0 = row * tokens * D + d;
-  int64_t t = 0;
-  for (; t + kCalUnroll <= tokens; t += kCalUnroll) {
+  CalAcc<SYM, MU, OCT> a{S[c], n[c], nullptr, 0u, So, no, c, nch};
+  if (OCT) {
+    uint32_t emax = 0;
+    int64_t t = t0;
+    for (; t + kCalUnroll <= t1; t += kCalUnroll) {
+      uint32_t mb[kCalUnroll];
+#pragma unroll
+      for (int u = 0; u < kCalUnroll; ++u) mb[u] = mload(i0 + (t + u) * D);
+#pragma unroll
+      for (int u = 0; u < kCalUnroll; ++u) emax = max(emax, mexp(mb[u]));
+    }
+    for (; t < t1; ++t) emax = max(emax, mexp(mload(i0 + t * D)));
+    // a finite mean has a field of at most 254, so the window ends by 254
+    a.base = emax >= (uint32_t)kOctWin ? emax - (kOctWin - 1) : 1u;
+    a.lds = reinterpret_cast<CalOctLds *>(&lds_oct);
+#pragma unroll
+    for (int s = 0; s < kOctSlots; ++s) {
+      const uint32_t e = s == kOctWin ? 0u : a.base + s;
+      a.lds->s[s][threadIdx.x] = So[(int64_t)e * nch + c];
+      a.lds->n[s][threadIdx.x] = 0;
+    }
+  }
+  int64_t t = t0;
+  for (; t + kCalUnroll <= t1; t += kCalUnroll) {
     uint32_t xb[kCalUnroll], mb[kCalUnroll];
 #pragma unroll
     for (int u = 0; u < kCalUnroll; ++u) {
@@ -122,9 +194,17 @@ __global__ __launch_bounds__(256) void k_calib_sums(const void *__restrict__ x, 
 #pragma unroll
     for (int u = 0; u < kCalUnroll; ++u) a.add(xb[u], mb[u]);
   }
-  for (; t < tokens; ++t) a.add(xload(i0 + t * D), mload(i0 + t * D));
+  for (; t < t1; ++t) a.add(xload(i0 + t * D), mload(i0 + t * D));
   S[c] = a.acc;
   n[c] = a.cnt;
+  if (OCT) {
+#pragma unroll
+    for (int s = 0; s < kOctSlots; ++s) {
+      const int64_t k = (int64_t)(s == kOctWin ? 0u : a.base + s) * nch + c;
+      So[k] = a.lds->s[s][threadIdx.x];
+      no[k] = no[k] + a.lds->n[s][threadIdx.x];
+    }
+  }
 }
 
 // Histogram: LDS counters for a window of 32768 bins, packed two 16-bit
@@ -158,19 +238,25 @@ __global__ __launch_bounds__(1024) void k_calib_hist(const void *__restrict__ x,
 hipError_t launch_calib_accumulate(const Geo &g, void *state, const void *x, const void *mu, hipStream_t st) {
   CalState cs = cal_state(g, state);
   int64_t nch = g.rows * g.D;
-  dim3 grid((unsigned)((nch + 255) / 256)), blk(256);
+  dim3 grid((unsigned)((nch + kCalThreads - 1) / kCalThreads)), blk(kCalThreads);
   const int sel = (g.sym_fmt == SKV_SYM_BF16 ? 0 : 4) + (g.mu_fmt == SKV_MU_BF16 ? 0 : 2) + g.octave;
-#define SKV_SUMS(S_, M_, O_) \
-  hipLaunchKernelGGL((k_calib_sums<S_, M_, O_>), grid, blk, 0, st, x, mu, cs.S, cs.n, cs.So, cs.no, g.rows, g.tokens, g.D)
-  switch (sel) {
-    case 0: SKV_SUMS(SKV_SYM_BF16, SKV_MU_BF16, 0); break;
-    case 1: SKV_SUMS(SKV_SYM_BF16, SKV_MU_BF16, 1); break;
-    case 2: SKV_SUMS(SKV_SYM_BF16, SKV_MU_F32, 0); break;
-    case 3: SKV_SUMS(SKV_SYM_BF16, SKV_MU_F32, 1); break;
-    case 4: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_BF16, 0); break;
-    case 5: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_BF16, 1); break;
-    case 6: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_F32, 0); break;
-    default: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_F32, 1); break;
+#define SKV_SUMS(S_, M_, O_)                                                                                      \
+  hipLaunchKernelGGL((k_calib_sums<S_, M_, O_>), grid, blk, 0, st, x, mu, cs.S, cs.n, cs.So, cs.no, g.rows, g.tokens, \
+                     g.D, t0, t1)
+  // octave mode counts a window bin in 32 bits: at most 2^31 tokens per launch
+  const int64_t seg = g.octave ? kOctSegTokens : g.tokens;
+  for (int64_t t0 = 0; t0 < g.tokens; t0 += seg) {
+    const int64_t t1 = g.tokens - t0 < seg ? g.tokens : t0 + seg;  // (HIP's host min() narrows to int)
+    switch (sel) {
+      case 0: SKV_SUMS(SKV_SYM_BF16, SKV_MU_BF16, 0); break;
+      case 1: SKV_SUMS(SKV_SYM_BF16, SKV_MU_BF16, 1); break;
+      case 2: SKV_SUMS(SKV_SYM_BF16, SKV_MU_F32, 0); break;
+      case 3: SKV_SUMS(SKV_SYM_BF16, SKV_MU_F32, 1); break;
+      case 4: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_BF16, 0); break;
+      case 5: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_BF16, 1); break;
+      case 6: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_F32, 0); break;
+      default: SKV_SUMS(SKV_SYM_E4M3, SKV_MU_F32, 1); break;
+    }
   }
 #undef SKV_SUMS
   int64_t total = g.rows * g.tokens * g.D;
@@ -232,8 +318,8 @@ __global__ void k_calib_finalize_oct(const double *__restrict__ S, const uint64_
   float *t = table + c * SKV_OCT_STRIDE;
   t[0] = sc;
   const int base = (int)((__float_as_uint(sc > 0x1p-100f ? sc : 0x1p-100f) >> 23) & 0xFFu) + 1;
-  const double *so = So + c * kExpBins;
-  const uint64_t *nn = no + c * kExpBins;
+  const double *so = So + c;  // bin e at so[e * nch]
+  const uint64_t *nn = no + c;
   for (int j = 0; j < kOctaves; ++j) {
     // exponent fields of octave j: [0, base] for j = 0, base + j for 0 < j < 7, [base + 7, 255] for j = 7
     const int e0 = j == 0 ? 0 : base + j;
@@ -241,8 +327,8 @@ __global__ void k_calib_finalize_oct(const double *__restrict__ S, const uint64_
     double sj = 0.0;
     uint64_t nj = 0;
     for (int e = e0; e <= e1 && e < kExpBins; ++e) {
-      sj = sj + so[e];
-      nj += nn[e];
+      sj = sj + so[(int64_t)e * nch];
+      nj += nn[(int64_t)e * nch];
     }
     t[1 + j] = nj < 16 ? sc : rn32_sqrt(sj / (double)nj);
   }

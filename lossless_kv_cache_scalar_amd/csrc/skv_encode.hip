@@ -458,6 +458,33 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
         s[j] = a.scale[ch].x;
       }
     }
+    // octave mode with at most two channels per lane (head_dim up to 128): the
+    // lane's whole scale table, 8 octaves per channel, sits in registers and
+    // a symbol picks its scale by three selects on the octave's bits. With
+    // the table in memory the next batch's scales are read half a batch
+    // ahead, and that read waits for the next batch's means, which have then
+    // had only half a batch to arrive (k_encode 18% slower on the FP8-residual
+    // cache). Wider heads would need 32 or 64 registers for the table and keep
+    // the reads.
+    constexpr bool kRegOct = OCT && PER <= 2;
+    static_assert(kOctaves == 8, "the scale select takes three octave bits");
+    float so[kRegOct ? PER * kOctaves : 1];
+    if (kRegOct) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+#pragma unroll
+        for (int q = 0; q < kOctaves; ++q) so[j * kOctaves + q] = srow[(q << lgD) + cb[j]].x;
+#pragma unroll
+      for (int q = 0; q < PER * kOctaves; ++q) asm volatile("" ::"v"(so[q]));
+    }
+    auto scale_reg = [&](float m, int j) {
+      const uint32_t o = octave_of(m, er[j % PER]);
+      const float *tb = so + (kRegOct ? (j % PER) * kOctaves : 0);
+      const bool o1 = (o & 1u) != 0, o2 = (o & 2u) != 0, o4 = (o & 4u) != 0;
+      const float a0 = o1 ? tb[1] : tb[0], a1 = o1 ? tb[3] : tb[2], a2 = o1 ? tb[5] : tb[4], a3 = o1 ? tb[7] : tb[6];
+      const float b0 = o2 ? a1 : a0, b1 = o2 ? a3 : a2;
+      return o4 ? b1 : b0;
+    };
     // wait for the scales here: a wait inside the symbol loop would also wait
     // for the batch loads in flight on every trip
 #pragma unroll
@@ -477,14 +504,15 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
     // two batch buffers used by turns (the next batch loads into the other
     // one), so no batch is copied from one set of registers to the other
     Batch<SYM, MU> bA, bB;
-    // octave mode: a batch's scales depend on its means; they are read half a
-    // batch ahead, once the next batch's means have arrived
+    // octave mode with the table in memory: a batch's scales depend on its
+    // means; they are read half a batch ahead, once the next batch's means
+    // have arrived
     float sA[kBatch], sB[kBatch];
     if (nfull > 0) {
       bA.load_full(a, base + lane);
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(bA.xs[j]), "v"(bA.ms[j]));
-      if (OCT) {
+      if (OCT && !kRegOct) {
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) sA[j] = scale_at(bA.mu(j), j);
       }
@@ -503,16 +531,17 @@ __device__ __forceinline__ void encode_chunks(const EncArgs &a, const EncTables 
       // (k_encode -1.5..-3% on the e4m3 caches and -1% on bf16 in A/B runs)
       cod.flush_batch();
       uint32_t c = 0, f = 0;
-      model_pair<SYM, FAST>(a, t, cur.xs[0], cur.mu(0), OCT ? sb[0] : s[0], c, f);
+      model_pair<SYM, FAST>(a, t, cur.xs[0], cur.mu(0), kRegOct ? scale_reg(cur.mu(0), 0) : OCT ? sb[0] : s[0], c, f);
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        if (OCT && j == kBatch / 2 && b + 1 < nfull) {
+        if (OCT && !kRegOct && j == kBatch / 2 && b + 1 < nfull) {
 #pragma unroll
           for (int q = 0; q < kBatch; ++q) sbn[q] = scale_at(nxt.mu(q), q);
         }
         uint32_t cn = 0, fn = 0;
         if (j + 1 < kBatch)
-          model_pair<SYM, FAST>(a, t, cur.xs[j + 1], cur.mu(j + 1), OCT ? sb[j + 1] : s[(j + 1) % PER], cn, fn);
+          model_pair<SYM, FAST>(a, t, cur.xs[j + 1], cur.mu(j + 1),
+                                kRegOct ? scale_reg(cur.mu(j + 1), j + 1) : OCT ? sb[j + 1] : s[(j + 1) % PER], cn, fn);
         cod.encode(c, f);
         c = cn;
         f = fn;
