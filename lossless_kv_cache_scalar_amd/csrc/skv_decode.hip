@@ -195,17 +195,21 @@ __device__ __forceinline__ uint32_t a_guess(const ModelTabs &t, uint32_t k) {
 // The symbol whose bin holds the value where the Gaussian pair's CDF reaches
 // t - A(k): the inverse table gives the knot coordinate, mu + u sigma / 64 the
 // value, and rounding to the symbol format the guess.  ts is t in steps of the
-// inverse table (kNInv / MG counts per step).  INTERP = false takes the table
-// point below t instead of interpolating (for a first e4m3 guess, whose only use
-// is the A of its bin: e4m3 bins are wide).
-template <int SYM, int TAB, bool INTERP = true>
+// inverse table (kNInv / MG counts per step).  A first guess, whose only use is
+// the A of its bin, takes a table point instead of interpolating within the
+// step: the point below t for e4m3 (kGuessFloor; its bins are wide), the
+// nearest one for bf16 (kGuessNearest).
+constexpr int kGuessInterp = 0, kGuessFloor = 1, kGuessNearest = 2;
+template <int SYM, int TAB, int MODE = kGuessInterp>
 __device__ __forceinline__ uint32_t guess_symbol(const ModelTabs &t, const float2 *uinv, float ts, uint32_t k,
                                                  float inv_step, float sinv, float m) {
   float mf = __builtin_fmaf((float)a_guess<SYM, TAB>(t, k), -inv_step, ts);
   mf = __builtin_fminf(__builtin_fmaxf(mf, 0.0f), (float)kNInv - 0.5f);
-  const int ii = (int)mf;  // mf >= 0: truncation is the floor
+  // mf >= 0: truncation is the floor; the nearest point is at most kNInv, the
+  // table's last entry
+  const int ii = MODE == kGuessNearest ? (int)(mf + 0.5f) : (int)mf;
   const float2 ud = uinv[ii];
-  const float uu = INTERP ? __builtin_fmaf(__builtin_amdgcn_fractf(mf), ud.y, ud.x) : ud.x;
+  const float uu = MODE == kGuessInterp ? __builtin_fmaf(__builtin_amdgcn_fractf(mf), ud.y, ud.x) : ud.x;
   const float e = __builtin_fmaf(uu, sinv, m);
   return SYM == SKV_SYM_BF16 ? bf16_rne_bits(e) : e4m3_rne_bits(e);
 }
@@ -421,10 +425,12 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   uint32_t kmu;
   if (BF) kmu = tix_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : mraw);
   else kmu = tix_e4m3(e4m3_rne_bits(m));
-  // e4m3: the first guess without interpolation (k_decode -1.4% on the 32K
-  // e4m3 cache, -2.7% on the 0.6B one; without it in both guesses +6%; bf16,
-  // whose bins near zero are narrow, gains nothing)
-  uint32_t gs = guess_symbol<SYM, TAB, BF>(t, uinv, ts, kmu, a.inv_step, sinvj, m);
+  // the first guess at a table point (A/B runs, k_decode: e4m3 with the point
+  // below t -1.4% on the 32K e4m3 cache and -2.7% on the 0.6B one, with the
+  // nearest point slower; bf16 with the nearest point -1.5% on the 32B cache,
+  // with the point below t unchanged; a second guess at a table point too
+  // +6% on e4m3)
+  uint32_t gs = guess_symbol<SYM, TAB, BF ? kGuessNearest : kGuessFloor>(t, uinv, ts, kmu, a.inv_step, sinvj, m);
   gs = guess_symbol<SYM, TAB>(t, uinv, ts, BF ? tix_bf16(gs) : tix_e4m3(gs), a.inv_step, sinvj, m);
   // ---- verify exactly
   uint32_t clo, chi;
