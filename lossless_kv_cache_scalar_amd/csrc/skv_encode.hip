@@ -197,6 +197,8 @@ struct LaneCoder {
   uint32_t *out;   // the lane's word 0 in the chunk's slot
   uint8_t *slot;   // the chunk's slot (the same for the whole wave)
   uint32_t off;    // byte offset of the lane's word nw in the slot
+  uint32_t q0, q1; // completed words not stored yet, oldest first: words nw - nq .. nw - 1
+  int nq;          // 0, 1 or 2
 
   __device__ __forceinline__ void init(uint8_t *chunk_slot, uint32_t lane, uint32_t cap_words) {
     X = 0;
@@ -208,6 +210,8 @@ struct LaneCoder {
     slot = chunk_slot;
     out = reinterpret_cast<uint32_t *>(chunk_slot) + lane;
     off = 4u * lane;
+    q0 = q1 = 0;
+    nq = 0;
   }
 
   // Stores the lane's oldest complete word, the one that starts at bit
@@ -220,11 +224,32 @@ struct LaneCoder {
     room += 32;
     off += 4u * kLanes;
   }
-  // Before a full batch: a word from every lane that has one, so that a lane
-  // holds at most 32 bits, and its symbols add at most 24 bits each.  Within
-  // the batch a lane stores again only when acc would overflow (a rare
-  // wave-wide branch); the slot sees each word written once, from one lane.
+  // A word completed within a batch waits in q0, q1 and is stored at the next
+  // batch's start (a third one stores the oldest at once).  Loads and stores
+  // share one counter, so the wait for a batch's symbols and means, issued a
+  // batch earlier, also waited for every store made since; a store late in a
+  // batch made the next batch wait for it (k_encode -1.5% on the 32B bf16
+  // cache, -1.2% on the 32K e4m3 cache in A/B runs).
+  __device__ __forceinline__ void queue_word() {
+    const uint32_t word = (uint32_t)(acc >> (32 - room));
+    if (nq == 2) *reinterpret_cast<uint32_t *>(slot + off - 8u * kLanes) = __builtin_bswap32(q0);
+    q0 = nq == 0 ? word : (nq == 2 ? q1 : q0);
+    q1 = nq >= 1 ? word : q1;
+    nq = nq < 2 ? nq + 1 : 2;
+    ++nw;
+    room += 32;
+    off += 4u * kLanes;
+  }
+  __device__ __forceinline__ void drain() {
+    if (nq >= 1) *reinterpret_cast<uint32_t *>(slot + off - 4u * kLanes * (uint32_t)nq) = __builtin_bswap32(q0);
+    if (nq == 2) *reinterpret_cast<uint32_t *>(slot + off - 4u * kLanes) = __builtin_bswap32(q1);
+    nq = 0;
+  }
+  // Before a full batch: the queued words, and a word from every lane that has
+  // one, so that a lane holds at most 32 bits, and its symbols add at most 24
+  // bits each.
   __device__ __forceinline__ void flush_batch() {
+    if (__any(nq > 0)) drain();
     if (__any(room <= 32)) {
       if (room <= 32) store_word();
     }
@@ -252,10 +277,13 @@ struct LaneCoder {
     const uint32_t n8 = __builtin_clz((uint32_t)(rg >> 16)) & 24u;
     // room for n8 more bits in acc (n8 > room implies room < 24: a word is complete)
     if (__builtin_expect(__any((int)n8 > room), 0)) {
-      if ((int)n8 > room) store_word();
+      if ((int)n8 > room) queue_word();
     }
     if (__builtin_expect(__any(carry), 0)) {
-      if (carry) acc = carry_out(acc, 64 - room, out, nw, capw);
+      if (carry) {
+        drain();  // the carry may reach the stored words
+        acc = carry_out(acc, 64 - room, out, nw, capw);
+      }
     }
     // the top n8 bits of X (width 0 reads as 0 whatever the offset)
     const uint32_t outb = __builtin_amdgcn_ubfe((uint32_t)(X >> 32), 32u - n8, n8);
@@ -270,6 +298,7 @@ struct LaneCoder {
     const uint64_t Xn = (X + (kTop40 - 1)) & ~(kTop40 - 1);
     const bool carry = Xn < X;
     X = Xn;
+    drain();
     if (carry) acc = carry_out(acc, 64 - room, out, nw, capw);
     while (room <= 32) store_word();
     acc = (acc << 24) | (X >> 40);
