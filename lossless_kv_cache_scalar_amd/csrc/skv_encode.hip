@@ -197,8 +197,8 @@ struct LaneCoder {
   uint32_t *out;   // the lane's word 0 in the chunk's slot
   uint8_t *slot;   // the chunk's slot (the same for the whole wave)
   uint32_t off;    // byte offset of the lane's word nw in the slot
-  uint32_t q0, q1; // completed words not stored yet, oldest first: words nw - nq .. nw - 1
-  int nq;          // 0, 1 or 2
+  uint32_t q0;     // a completed word not stored yet: word nw - 1 when held
+  bool held;
 
   __device__ __forceinline__ void init(uint8_t *chunk_slot, uint32_t lane, uint32_t cap_words) {
     X = 0;
@@ -210,8 +210,8 @@ struct LaneCoder {
     slot = chunk_slot;
     out = reinterpret_cast<uint32_t *>(chunk_slot) + lane;
     off = 4u * lane;
-    q0 = q1 = 0;
-    nq = 0;
+    q0 = 0;
+    held = false;
   }
 
   // Stores the lane's oldest complete word, the one that starts at bit
@@ -224,32 +224,31 @@ struct LaneCoder {
     room += 32;
     off += 4u * kLanes;
   }
-  // A word completed within a batch waits in q0, q1 and is stored at the next
-  // batch's start (a third one stores the oldest at once).  Loads and stores
+  // A word completed within a batch waits in q0 and is stored at the next
+  // batch's start (a second one stores the first at once).  Loads and stores
   // share one counter, so the wait for a batch's symbols and means, issued a
   // batch earlier, also waited for every store made since; a store late in a
-  // batch made the next batch wait for it (k_encode -1.5% on the 32B bf16
-  // cache, -1.2% on the 32K e4m3 cache in A/B runs).
+  // batch made the next batch wait for it (k_encode -4.8% on the 32B bf16
+  // cache, -1.2% on the 32K e4m3 cache in A/B runs; holding two words cost
+  // more selects and saved less).
   __device__ __forceinline__ void queue_word() {
     const uint32_t word = (uint32_t)(acc >> (32 - room));
-    if (nq == 2) *reinterpret_cast<uint32_t *>(slot + off - 8u * kLanes) = __builtin_bswap32(q0);
-    q0 = nq == 0 ? word : (nq == 2 ? q1 : q0);
-    q1 = nq >= 1 ? word : q1;
-    nq = nq < 2 ? nq + 1 : 2;
+    if (held) *reinterpret_cast<uint32_t *>(slot + off - 4u * kLanes) = __builtin_bswap32(q0);
+    q0 = word;
+    held = true;
     ++nw;
     room += 32;
     off += 4u * kLanes;
   }
   __device__ __forceinline__ void drain() {
-    if (nq >= 1) *reinterpret_cast<uint32_t *>(slot + off - 4u * kLanes * (uint32_t)nq) = __builtin_bswap32(q0);
-    if (nq == 2) *reinterpret_cast<uint32_t *>(slot + off - 4u * kLanes) = __builtin_bswap32(q1);
-    nq = 0;
+    if (held) *reinterpret_cast<uint32_t *>(slot + off - 4u * kLanes) = __builtin_bswap32(q0);
+    held = false;
   }
   // Before a full batch: the queued words, and a word from every lane that has
   // one, so that a lane holds at most 32 bits, and its symbols add at most 24
   // bits each.
   __device__ __forceinline__ void flush_batch() {
-    if (__any(nq > 0)) drain();
+    if (__any(held)) drain();
     if (__any(room <= 32)) {
       if (room <= 32) store_word();
     }
