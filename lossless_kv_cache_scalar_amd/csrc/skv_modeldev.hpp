@@ -18,8 +18,9 @@ __device__ __forceinline__ uint64_t mul24(uint32_t a, uint32_t b) {
 }
 
 // Where the bf16 p_hat table A lives for a kernel.
-enum { kTabGlobal = 0,   // A from global memory only (the 16-bit window image does not fit)
-       kTabLdsAll = 1 }; // all 1024 windows in LDS
+enum { kTabGlobal = 0,    // A from global memory only (the 16-bit window image does not fit)
+       kTabLdsAll = 1,    // all 1024 windows in LDS
+       kTabPattern = 2 }; // static e4m3: bins and (A(k), A(k + 1)) in one table by pattern
 
 struct ModelTabs {
   const float2 *kn;      // LDS: knots (K_j, D_j)
@@ -27,6 +28,7 @@ struct ModelTabs {
   const uint32_t *ab;    // LDS: window bases (bf16); e4m3: (A(k), A(k + 1)) at 2 tix_e4m3, 2 tix_e4m3 + 1
   const uint32_t *ptab;  // global: full table A in rank order
   const float2 *et;      // LDS: e4m3 bins
+  const float4 *ep;      // LDS, kTabPattern: per e4m3 pattern (lower edge, upper edge, A(k), A(k + 1))
 };
 
 // A(k) and A(k + 1) of bf16 rank k, given as its table index ti = k ^ 0x8000
@@ -84,6 +86,10 @@ __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float
         chi = ahi + cg_eval(t.kn, u_of(hi, m, s));
       }
     }
+  } else if (TAB == kTabPattern) {
+    const float4 q = t.ep[b];
+    clo = __float_as_uint(q.z) + cg_eval(t.kn, u_of(q.x, m, s));
+    chi = __float_as_uint(q.w) + cg_eval(t.kn, u_of(q.y, m, s));
   } else {
     const float2 e = t.et[b];
     const uint2 p = reinterpret_cast<const uint2 *>(t.ab)[tix_e4m3(b)];
@@ -108,6 +114,10 @@ __device__ __forceinline__ uint32_t cum_rank(const ModelTabs &t, uint32_t k, flo
     return a_one<TAB>(t, k ^ 0x8000u) + cg_eval(t.kn, u_of(__uint_as_float(e), m, s));
   } else {
     if (k >= 256u) return 1u << 16;
+    if (TAB == kTabPattern) {
+      const float4 q = t.ep[unrank_e4m3(k)];
+      return __float_as_uint(q.z) + cg_eval(t.kn, u_of(q.x, m, s));
+    }
     return t.ab[2u * (k ^ 0x80u)] + cg_eval(t.kn, u_of(t.et[unrank_e4m3(k)].x, m, s));
   }
 }
