@@ -185,7 +185,7 @@ __device__ __forceinline__ uint32_t e4m3_rne_bits(float e) {
   return v;
 }
 
-// A(k) for a guess; k is the table index (tix_bf16 or tix_e4m3)
+// A(k) for a guess; k is the table index (bf16: tix_bf16; e4m3: the pattern)
 template <int SYM, int TAB>
 __device__ __forceinline__ uint32_t a_guess(const ModelTabs &t, uint32_t k) {
   if (SYM != SKV_SYM_BF16) return TAB == kTabPattern ? __float_as_uint(t.ep[k].z) : t.ab[2u * k];
@@ -424,15 +424,14 @@ __device__ __forceinline__ uint32_t decode_symbol(const DecArgs &a, const ModelT
   // (any start serves: a non-finite bf16 mean starts from its own pattern)
   uint32_t kmu;
   if (BF) kmu = tix_bf16(MU == SKV_MU_F32 ? bf16_rne_bits(m) : mraw);
-  else kmu = TAB == kTabPattern ? e4m3_rne_bits(m) : tix_e4m3(e4m3_rne_bits(m));
+  else kmu = e4m3_rne_bits(m);
   // the first guess at a table point (A/B runs, k_decode: e4m3 with the point
   // below t -1.4% on the 32K e4m3 cache and -2.7% on the 0.6B one, with the
   // nearest point slower; bf16 with the nearest point -1.5% on the 32B cache,
   // with the point below t unchanged; a second guess at a table point too
   // +6% on e4m3)
   uint32_t gs = guess_symbol<SYM, TAB, BF ? kGuessNearest : kGuessFloor>(t, uinv, ts, kmu, a.inv_step, sinvj, m);
-  gs = guess_symbol<SYM, TAB>(t, uinv, ts, BF ? tix_bf16(gs) : (TAB == kTabPattern ? gs : tix_e4m3(gs)), a.inv_step,
-                              sinvj, m);
+  gs = guess_symbol<SYM, TAB>(t, uinv, ts, BF ? tix_bf16(gs) : gs, a.inv_step, sinvj, m);
   // ---- verify exactly
   uint32_t clo, chi;
   uint64_t dd, pf;
@@ -701,8 +700,8 @@ void k_decode(DecArgs a) {
       for (int i = threadIdx.x; i <= kNWin; i += kB) s_ab[i] = a.abase[i];
     }
   } else if (AD) {
-    // (A(k), A(k + 1)) side by side at table index k ^ 0x80
-    for (int i = threadIdx.x; i < 512; i += kB) s_ab[i] = a.ptab[((uint32_t)i >> 1 ^ 0x80u) + (i & 1)];
+    // (A(k), A(k + 1)) side by side at the pattern of rank k
+    for (int i = threadIdx.x; i < 512; i += kB) s_ab[i] = a.ptab[(tix_e4m3((uint32_t)i >> 1) ^ 0x80u) + (i & 1)];
     for (int i = threadIdx.x; i < 256; i += kB) s_et[i] = a.etab[i];
   } else {
     for (int i = threadIdx.x; i < 256; i += kB) {

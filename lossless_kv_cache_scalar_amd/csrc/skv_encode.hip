@@ -396,7 +396,7 @@ __device__ __forceinline__ void model_common(const EncArgs &a, const EncTables &
       p = make_uint2(__float_as_uint(q.z), __float_as_uint(q.w));
     } else {
       e = t.et[b];
-      p = reinterpret_cast<const uint2 *>(t.ab)[tix_e4m3(b)];
+      p = reinterpret_cast<const uint2 *>(t.ab)[b];
     }
     const uint32_t lo = p.x + cg_eval(t.kn, u_of(e.x, m, sj));
     const uint32_t hi = p.y + cg_eval(t.kn, u_of(e.y, m, sj));
@@ -714,8 +714,8 @@ __global__ __launch_bounds__(kEncBlock) void k_encode(EncArgs a) {
       for (int i = threadIdx.x; i <= kNWin; i += kEncBlock) s_ab[i] = a.abase[i];
     }
   } else {
-    // (A(k), A(k + 1)) side by side at table index k ^ 0x80
-    for (int i = threadIdx.x; i < 512; i += kEncBlock) s_ab[i] = a.ptab[((uint32_t)i >> 1 ^ 0x80u) + (i & 1)];
+    // (A(k), A(k + 1)) side by side at the pattern of rank k
+    for (int i = threadIdx.x; i < 512; i += kEncBlock) s_ab[i] = a.ptab[(tix_e4m3((uint32_t)i >> 1) ^ 0x80u) + (i & 1)];
     for (int i = threadIdx.x; i < 256; i += kEncBlock) s_et[i] = a.etab[i];
     if constexpr (AD == 0) {
       for (int i = threadIdx.x; i < 256; i += kEncBlock) {

@@ -162,8 +162,8 @@ __global__ __launch_bounds__(kPtBlock) void k_ptable(const uint64_t *__restrict_
 // rank scaled to the prior weight, C_0(k) = floor(SKV_ADAPT_PRIOR_WEIGHT
 // (A(k+1) - A(k) - 1) / Mp).  Stored already decayed, floor(alpha C_0(k)):
 // the counts a chunk's first epoch adds its symbols to, so that the table of
-// epoch 1 is built from C_1 = floor(alpha C_0) + n_0.  Index k ^ 0x80, as in
-// the kernels' count tables.
+// epoch 1 is built from C_1 = floor(alpha C_0) + n_0.  Stored at the
+// pattern of rank k, as the kernels' count tables are.
 __global__ void k_prior(const uint32_t *__restrict__ A, uint32_t *__restrict__ prior, uint32_t Mp) {
   const uint32_t k = threadIdx.x;
   if (k >= 256) return;

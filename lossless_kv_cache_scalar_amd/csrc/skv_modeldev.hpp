@@ -25,7 +25,7 @@ enum { kTabGlobal = 0,    // A from global memory only (the 16-bit window image 
 struct ModelTabs {
   const float2 *kn;      // LDS: knots (K_j, D_j)
   const uint16_t *a16;   // LDS: window image (bf16), window slots as tix_bf16 orders them
-  const uint32_t *ab;    // LDS: window bases (bf16); e4m3: (A(k), A(k + 1)) at 2 tix_e4m3, 2 tix_e4m3 + 1
+  const uint32_t *ab;    // LDS: window bases (bf16); e4m3: (A(k), A(k + 1)) at 2 b, 2 b + 1 for the pattern b of rank k
   const uint32_t *ptab;  // global: full table A in rank order
   const float2 *et;      // LDS: e4m3 bins
   const float4 *ep;      // LDS, kTabPattern: per e4m3 pattern (lower edge, upper edge, A(k), A(k + 1))
@@ -92,7 +92,7 @@ __device__ __forceinline__ void model_pair(const ModelTabs &t, uint32_t b, float
     chi = __float_as_uint(q.w) + cg_eval(t.kn, u_of(q.y, m, s));
   } else {
     const float2 e = t.et[b];
-    const uint2 p = reinterpret_cast<const uint2 *>(t.ab)[tix_e4m3(b)];
+    const uint2 p = reinterpret_cast<const uint2 *>(t.ab)[b];
     clo = p.x + cg_eval(t.kn, u_of(e.x, m, s));
     chi = p.y + cg_eval(t.kn, u_of(e.y, m, s));
   }
@@ -118,7 +118,8 @@ __device__ __forceinline__ uint32_t cum_rank(const ModelTabs &t, uint32_t k, flo
       const float4 q = t.ep[unrank_e4m3(k)];
       return __float_as_uint(q.z) + cg_eval(t.kn, u_of(q.x, m, s));
     }
-    return t.ab[2u * (k ^ 0x80u)] + cg_eval(t.kn, u_of(t.et[unrank_e4m3(k)].x, m, s));
+    const uint32_t pb = unrank_e4m3(k);
+    return t.ab[2u * pb] + cg_eval(t.kn, u_of(t.et[pb].x, m, s));
   }
 }
 
